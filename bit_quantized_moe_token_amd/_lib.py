@@ -1,0 +1,97 @@
+"""ctypes declarations of libmoeq's C ABI (include/moeq.h).
+
+Argument marshalling only: every computation happens in the HIP library.
+Loading fails loudly when the library has not been built.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+FMT_INT, FMT_BITPLANE = 0, 1
+F16, F32 = 0, 1
+PATH_AUTO, PATH_STREAM, PATH_VALU, PATH_TILED = 0, 1, 2, 3
+
+c_void_p = ctypes.c_void_p
+c_size_t = ctypes.c_size_t
+c_i32 = ctypes.c_int32
+c_u8p = ctypes.POINTER(ctypes.c_uint8)
+c_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("E", c_i32), ("H", c_i32), ("I", c_i32), ("G", c_i32),
+        ("fmt", c_i32),
+        ("bits", c_u8p),
+        ("codes", c_vpp), ("scales", c_vpp), ("zeros", c_vpp), ("luts", c_vpp),
+        ("r", c_i32), ("U", c_vpp), ("V", c_vpp),
+        ("rs", c_i32), ("share", c_i32), ("Us", c_vpp), ("Vs", c_vpp),
+    ]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [("topk_ids", c_void_p), ("topk_gates", c_void_p),
+                ("expert_offsets", c_void_p), ("sorted_pairs", c_void_p),
+                ("pair_pos", c_void_p)]
+
+
+class FfnOptions(ctypes.Structure):
+    _fields_ = [("path", c_i32), ("split_k", c_i32)]
+
+
+# (name, restype, argtypes) of every exported entry point
+SIGNATURES = [
+    ("moeq_status_string", ctypes.c_char_p, [c_i32]),
+    ("moeq_last_error", ctypes.c_char_p, []),
+    ("moeq_abi_version", c_i32, []),
+    ("moeq_quantize_rtn", c_i32, [c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    ("moeq_build_lut", c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p, c_void_p]),
+    ("moeq_pack_size", c_i32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(c_size_t)]),
+    ("moeq_pack", c_i32, [ctypes.POINTER(LayerDesc), c_void_p, c_size_t, c_void_p, ctypes.POINTER(c_void_p)]),
+    ("moeq_layer_destroy", None, [c_void_p]),
+    ("moeq_layer_block_bytes", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
+    ("moeq_layer_shared_bytes", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
+    ("moeq_debug_unpack", c_i32, [c_void_p, c_i32, c_i32, c_void_p, c_void_p]),
+    ("moeq_route_workspace_size", c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
+    ("moeq_route", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing), c_void_p, c_size_t, c_void_p]),
+    ("moeq_ffn_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions), ctypes.POINTER(c_size_t)]),
+    ("moeq_expert_ffn", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
+                                c_void_p, c_i32, c_void_p, c_size_t, ctypes.POINTER(FfnOptions), c_void_p]),
+    ("moeq_profile_enable", c_i32, [c_i32]),
+    ("moeq_profile_read", c_i32, [c_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_i32),
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32)]),
+]
+
+_lib = None
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {detail}")
+
+
+def lib():
+    """The loaded libmoeq (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmoeq.so not built at {LIB_PATH}; run "
+                              "python -m bit_quantized_moe_token_amd.build")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def check(status, where):
+    if status != OK:
+        detail = lib().moeq_last_error().decode(errors="replace")
+        raise MoeqError(status, where, detail)

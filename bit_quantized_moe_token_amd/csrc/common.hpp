@@ -1,0 +1,120 @@
+// Shared device/host definitions of libmoeq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moeq.h"
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace moeq {
+
+// --------------------------------------------------------------- layout --
+// Weights of one block (N x K) are stored in strips of 16 rows and tiles of
+// 128 columns.  A 16 x 128 tile is read by one wave: lane l owns row
+// n = l % 16 and the columns 32*j + 8*(l/16) + i (j = 0..3, i = 0..7), which
+// is the B-operand layout of v_mfma_f32_16x16x32_f16 for four consecutive
+// 32-column steps j.  Tiles are grouped by four so that each lane reads its
+// data for four tiles with 128-bit loads.
+constexpr int kStripRows = 16;
+constexpr int kTileK = 128;
+constexpr int kTilesPerGroup = 4;
+constexpr int kWave = 64;
+
+// Per-block record in device memory, written by moeq_pack.
+struct BlockDesc {
+  const uint8_t *codes;   // INT codes, or bit-plane 3 (MSB) of 4 planes
+  uint64_t plane_bytes;   // bytes of one bit-plane region (bit-plane form)
+  const uint16_t *scales; // tiled fp16 scales (INT)
+  const uint8_t *zeros;   // tiled zeros (INT)
+  const uint16_t *lut;    // tiled LUT, 2^q fp16 per (row, tile) (bit-plane)
+  const uint16_t *U;      // per-expert U [N, r] (nullptr when r == 0)
+  const uint16_t *V;      // per-expert V [r, K]
+  const uint16_t *Us;     // shared U of this expert's group [N, rs] or nullptr
+  const uint16_t *Vs;     // shared V [rs, K]
+  int32_t N, K, bits, fmt;
+};
+
+struct LayerDims {
+  int32_t E, H, I, G, fmt, r, rs, share;
+};
+
+// Host-side error reporting (thread local).
+void set_error(const char *fmt, ...);
+moeq_status fail(moeq_status s, const char *fmt, ...);
+moeq_status check_launch(const char *what);
+
+// Profiling hooks around launches (no-ops unless enabled).
+void prof_begin(const char *name, hipStream_t s);
+void prof_end(const char *name, hipStream_t s);
+
+// ------------------------------------------------------ device helpers --
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return (a & m) | c;   // v_and_or_b32
+}
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Round a float64 to the nearest fp16 (ties to even), directly from the
+// double's bits so there is exactly one rounding.  Finite inputs only.
+__host__ __device__ inline uint16_t f64_to_f16_bits(double d) {
+  uint64_t b;
+  __builtin_memcpy(&b, &d, 8);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  int exp = (int)((b >> 52) & 0x7ff);
+  uint64_t mant = b & ((1ull << 52) - 1);
+  if (exp == 0) return sign;                      // zero or double subnormal
+  int e = exp - 1023;                             // unbiased
+  if (e > 15) return sign | 0x7c00u;              // overflow -> inf
+  uint64_t sig = mant | (1ull << 52);             // 53-bit significand
+  int shift;                                      // bits to drop
+  uint32_t hexp;
+  if (e >= -14) {                                 // normal fp16
+    shift = 42;
+    hexp = (uint32_t)(e + 15);
+  } else {                                        // subnormal fp16
+    shift = 42 + (-14 - e);
+    hexp = 0;
+    if (shift > 53 + 1) return sign;              // rounds to zero
+  }
+  uint64_t q = sig >> shift;
+  uint64_t rem = sig & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) q += 1;
+  uint32_t out;
+  if (hexp == 0) {
+    out = (uint32_t)q;                            // may carry into exponent 1
+  } else {
+    // q holds the implicit bit at position 10; carry may bump the exponent
+    out = (hexp << 10) + (uint32_t)(q - (1u << 10));
+    if (q >= (1u << 11)) out = ((hexp + 1) << 10);
+  }
+  if (out >= 0x7c00u) out = 0x7c00u;
+  return sign | (uint16_t)out;
+}
+
+__host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
+  uint32_t sign = h >> 15, exp = (h >> 10) & 0x1f, mant = h & 0x3ff;
+  double v;
+  if (exp == 0) v = (double)mant * (1.0 / 16777216.0);               // 2^-24
+  else if (exp == 31) v = mant ? __builtin_nan("") : __builtin_inf();
+  else v = (double)(mant | 0x400) * __builtin_ldexp(1.0, (int)exp - 25);
+  return sign ? -v : v;
+}
+
+}  // namespace moeq
+
+#define MOEQ_API extern "C" __attribute__((visibility("default")))

@@ -1,0 +1,48 @@
+// Packed-layer handle and tiled-layout index helpers (host + device).
+#pragma once
+#include <vector>
+#include "common.hpp"
+
+namespace moeq {
+
+// Bytes per lane per tile of the code region: 4*b for INT, 4 per bit-plane.
+__host__ __device__ inline int lane_tile_bytes(int fmt, int bits) {
+  return fmt == MOEQ_FMT_INT ? 4 * bits : 4;
+}
+
+// Byte offset of lane l's data for tile t of strip s in a code region whose
+// lanes hold W bytes per tile.  Tiles are grouped by four; inside a group a
+// lane's bytes for the group's tiles are contiguous.
+__host__ __device__ inline uint64_t code_offset(int s, int t, int l, int n_kt, int W) {
+  const int g4 = t >> 2, tl = t & 3;
+  const int c = (n_kt - 4 * g4) < 4 ? (n_kt - 4 * g4) : 4;
+  return (uint64_t)s * n_kt * 64 * W + (uint64_t)g4 * 256 * W + (uint64_t)l * c * W +
+         (uint64_t)tl * W;
+}
+
+// Element index of the scale / zero of (strip s, tile t, row r, group gi in
+// the tile); gpt = groups per tile (128 / G).
+__host__ __device__ inline uint64_t meta_index(int s, int t, int r, int gi, int n_kt, int gpt) {
+  const int g4 = t >> 2, tl = t & 3;
+  const int c = (n_kt - 4 * g4) < 4 ? (n_kt - 4 * g4) : 4;
+  return (uint64_t)s * n_kt * 16 * gpt + (uint64_t)g4 * 64 * gpt + (uint64_t)r * c * gpt +
+         (uint64_t)tl * gpt + gi;
+}
+
+// Element index of LUT entry j of (strip s, tile t, row r); nq = 2^q.
+__host__ __device__ inline uint64_t lut_index(int s, int t, int r, int j, int n_kt, int nq) {
+  return ((uint64_t)s * n_kt + t) * 16 * nq + (uint64_t)r * nq + j;
+}
+
+}  // namespace moeq
+
+struct moeq_layer {
+  moeq::LayerDims dims;
+  uint8_t *buf;
+  size_t bytes;
+  moeq::BlockDesc *d_desc;                 // device table (inside buf)
+  std::vector<moeq::BlockDesc> h_desc;     // host copy of the table
+  std::vector<uint8_t> bits;               // [E*3]
+  std::vector<size_t> block_alg_bytes;     // [E*3]
+  std::vector<size_t> shared_alg_bytes;    // [groups*3]
+};

@@ -1,0 +1,234 @@
+"""Python binding of libmoeq over torch device tensors.
+
+torch provides device memory and the current HIP stream; each function below
+validates shapes, passes raw pointers to the C ABI and returns the tensors
+the library filled.  No arithmetic of the method happens here.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+GATE, UP, DOWN = 0, 1, 2
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------- encoding
+
+def quantize_rtn(w, bits, G):
+    """Asymmetric RTN of an fp16 block [N, K]: (codes u8 [N,K], scales fp16
+    [N,K/G], zeros u8 [N,K/G])."""
+    N, K = w.shape
+    _need(w, torch.float16, (N, K), "w")
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // G), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((N, K // G), dtype=torch.uint8, device=w.device)
+    check(lib().moeq_quantize_rtn(_ptr(w), N, K, G, bits, _ptr(codes), _ptr(scales), _ptr(zeros),
+                                  _stream()), "moeq_quantize_rtn")
+    return codes, scales, zeros
+
+
+def build_lut(w, codes4, scales, zeros, q, G):
+    """16-slot fp16 LUT [N, K/G, 16] of a block committed to q bit-planes."""
+    N, K = w.shape
+    _need(w, torch.float16, (N, K), "w")
+    _need(codes4, torch.uint8, (N, K), "codes4")
+    _need(scales, torch.float16, (N, K // G), "scales")
+    _need(zeros, torch.uint8, (N, K // G), "zeros")
+    lut = torch.empty((N, K // G, 16), dtype=torch.float16, device=w.device)
+    check(lib().moeq_build_lut(_ptr(w), _ptr(codes4), _ptr(scales), _ptr(zeros), N, K, G, q,
+                               _ptr(lut), _stream()), "moeq_build_lut")
+    return lut
+
+
+# ---------------------------------------------------------------- layer
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr() if t is not None else 0
+    return arr
+
+
+class PackedLayer:
+    """A packed quantized layer: one device buffer plus the library handle.
+
+    blocks: list over b = e*3 + blk of dicts with
+      INT:      codes u8 [N,K], scales fp16 [N,K/G], zeros u8 [N,K/G]
+      bitplane: codes (4-bit parent codes) u8 [N,K], lut fp16 [N,K/G,16]
+    factors: list over b of (U [N,r], V [r,K]) fp16 or None (r = 0)
+    shared: list over group*3+blk of (Us, Vs) or None (rs = 0)
+    """
+
+    def __init__(self, E, H, I, G, fmt, bits, blocks, factors=None, shared=None, share=0,
+                 device=None):
+        device = device or torch.device("cuda", torch.cuda.current_device())
+        self.E, self.H, self.I, self.G = E, H, I, G
+        self.fmt = fmt
+        self.bits = np.asarray(bits, dtype=np.uint8).reshape(E * 3).copy()
+        nb = 3 * E
+        assert len(blocks) == nb
+        fmt_id = _lib.FMT_INT if fmt == "int" else _lib.FMT_BITPLANE
+        self._keep = []
+        codes = _ptr_array([b["codes"] for b in blocks])
+        if fmt == "int":
+            scales = _ptr_array([b["scales"] for b in blocks])
+            zeros = _ptr_array([b["zeros"] for b in blocks])
+            luts = None
+        else:
+            scales = zeros = None
+            luts = _ptr_array([b["lut"] for b in blocks])
+        r = 0
+        U = V = None
+        if factors is not None and factors[0] is not None:
+            r = factors[0][0].shape[1]
+            U = _ptr_array([f[0] for f in factors])
+            V = _ptr_array([f[1] for f in factors])
+        rs = 0
+        Us = Vs = None
+        if shared is not None and shared[0] is not None:
+            rs = shared[0][0].shape[1]
+            Us = _ptr_array([f[0] for f in shared])
+            Vs = _ptr_array([f[1] for f in shared])
+        self.r, self.rs, self.share = r, rs, share
+        bits_arr = (ctypes.c_uint8 * nb)(*[int(b) for b in self.bits])
+        cast = lambda a: ctypes.cast(a, _lib.c_vpp) if a is not None else None
+        d = _lib.LayerDesc(E, H, I, G, fmt_id, ctypes.cast(bits_arr, _lib.c_u8p), cast(codes),
+                           cast(scales), cast(zeros), cast(luts), r, cast(U), cast(V), rs, share,
+                           cast(Us), cast(Vs))
+        self._desc_keep = (bits_arr, codes, scales, zeros, luts, U, V, Us, Vs)
+        nbytes = ctypes.c_size_t(0)
+        check(lib().moeq_pack_size(ctypes.byref(d), ctypes.byref(nbytes)), "moeq_pack_size")
+        self.buf = torch.empty(nbytes.value, dtype=torch.uint8, device=device)
+        handle = ctypes.c_void_p(0)
+        check(lib().moeq_pack(ctypes.byref(d), _ptr(self.buf), nbytes.value, _stream(),
+                              ctypes.byref(handle)), "moeq_pack")
+        self.handle = handle
+        self.nbytes = nbytes.value
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.moeq_layer_destroy(h)
+            self.handle = None
+
+    def block_bytes(self, e, blk):
+        out = ctypes.c_size_t(0)
+        check(lib().moeq_layer_block_bytes(self.handle, e, blk, ctypes.byref(out)), "block_bytes")
+        return out.value
+
+    def shared_bytes(self, g, blk):
+        out = ctypes.c_size_t(0)
+        check(lib().moeq_layer_shared_bytes(self.handle, g, blk, ctypes.byref(out)), "shared_bytes")
+        return out.value
+
+    def block_shape(self, blk):
+        return (self.I, self.H) if blk in (GATE, UP) else (self.H, self.I)
+
+    def debug_unpack(self, e, blk):
+        N, K = self.block_shape(blk)
+        out = torch.empty((N, K), dtype=torch.uint8, device=self.buf.device)
+        check(lib().moeq_debug_unpack(self.handle, e, blk, _ptr(out), _stream()), "moeq_debug_unpack")
+        return out
+
+
+def quantize_block(w, fmt, bits, G):
+    """Quantize one fp16 block with the library's kernels into the pack input
+    dict (INT: codes/scales/zeros; bit-plane: 4-bit parent codes + LUT)."""
+    if fmt == "int":
+        c, s, z = quantize_rtn(w, bits, G)
+        return dict(codes=c, scales=s, zeros=z)
+    c, s, z = quantize_rtn(w, 4, G)
+    return dict(codes=c, lut=build_lut(w, c, s, z, bits, G))
+
+
+# -------------------------------------------------------------- routing
+
+class RoutingOut:
+    def __init__(self, T, E, k, device):
+        self.T, self.E, self.k = T, E, k
+        P = T * k
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+        self.sorted_pairs = torch.empty((P,), dtype=torch.int32, device=device)
+        self.pair_pos = torch.empty((P,), dtype=torch.int32, device=device)
+        self.c = _lib.Routing(self.ids.data_ptr(), self.gates.data_ptr(), self.offsets.data_ptr(),
+                              self.sorted_pairs.data_ptr(), self.pair_pos.data_ptr())
+
+
+def route(logits, k, out=None):
+    """Top-k routing and counting sort of fp32 logits [T, E] (see moeq_route)."""
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    if out is None:
+        out = RoutingOut(T, E, k, logits.device)
+    check(lib().moeq_route(_ptr(logits), T, E, k, ctypes.byref(out.c), None, 0, _stream()), "moeq_route")
+    return out
+
+
+# ------------------------------------------------------------ expert FFN
+
+class FfnWorkspace:
+    def __init__(self, layer, T, k, path=0, split_k=0):
+        self.opts = _lib.FfnOptions(path, split_k)
+        n = ctypes.c_size_t(0)
+        check(lib().moeq_ffn_workspace_size(layer.handle, T, k, ctypes.byref(self.opts), ctypes.byref(n)),
+              "moeq_ffn_workspace_size")
+        self.nbytes = n.value
+        self.buf = torch.empty(max(256, n.value), dtype=torch.uint8, device=layer.buf.device)
+
+
+def expert_ffn(layer, x, routing, n_comp, out=None, out_dtype=torch.float16, ws=None, path=0,
+               split_k=0):
+    """Routed expert FFN y [T, H] (see moeq_expert_ffn)."""
+    T = routing.T
+    k = routing.k
+    _need(x, torch.float16, (T, layer.H), "x")
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=out_dtype, device=x.device)
+    ydt = _lib.F32 if out.dtype == torch.float32 else _lib.F16
+    _need(out, out.dtype, (T, layer.H), "out")
+    if ws is None:
+        ws = FfnWorkspace(layer, T, k, path, split_k)
+    check(lib().moeq_expert_ffn(layer.handle, _ptr(x), T, k, ctypes.byref(routing.c), n_comp,
+                                _ptr(out), ydt, _ptr(ws.buf), ws.buf.numel(), ctypes.byref(ws.opts),
+                                _stream()), "moeq_expert_ffn")
+    return out
+
+
+# ------------------------------------------------------------ profiling
+
+def profile_enable(on=True):
+    check(lib().moeq_profile_enable(1 if on else 0), "moeq_profile_enable")
+
+
+def profile_read(max_kernels=64):
+    names = (ctypes.c_char_p * max_kernels)()
+    launches = (ctypes.c_int32 * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    n = ctypes.c_int32(0)
+    check(lib().moeq_profile_read(max_kernels, names, launches, ms, ctypes.byref(n)), "moeq_profile_read")
+    return {names[i].decode(): (int(launches[i]), float(ms[i])) for i in range(min(n.value, max_kernels))}

@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host (no device work)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moeq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_quantized_moe_token_amd import _lib
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_covers_header():
+    from bit_quantized_moe_token_amd import _lib
+    bound = {s[0] for s in _lib.SIGNATURES}
+    assert set(_declared()) == bound
+
+
+def test_status_strings(L):
+    assert L.moeq_status_string(0) == b"MOEQ_OK"
+    assert L.moeq_status_string(3) == b"MOEQ_ERR_WORKSPACE"
+    assert L.moeq_abi_version() >= 1
+
+
+def _err(L):
+    return L.moeq_last_error().decode()
+
+
+def test_quantize_validation(L):
+    p = ctypes.c_void_p(16)
+    assert L.moeq_quantize_rtn(p, 4, 64, 64, 5, p, p, p, None) == 1
+    assert "bits" in _err(L)
+    assert L.moeq_quantize_rtn(p, 4, 64, 48, 4, p, p, p, None) == 1
+    assert L.moeq_quantize_rtn(None, 4, 64, 64, 4, p, p, p, None) == 1
+    assert L.moeq_build_lut(p, p, p, p, 4, 128, 128, 5, p, None) == 1
+
+
+def test_route_validation(L):
+    from bit_quantized_moe_token_amd import _lib
+    r = _lib.Routing(16, 16, 16, 16, 16)
+    assert L.moeq_route(ctypes.c_void_p(16), 4, 8, 9, ctypes.byref(r), None, 0, None) == 1
+    assert L.moeq_route(ctypes.c_void_p(16), 4, 300, 2, ctypes.byref(r), None, 0, None) == 1
+    assert L.moeq_route(ctypes.c_void_p(16), -1, 8, 2, ctypes.byref(r), None, 0, None) == 1
+    n = ctypes.c_size_t(7)
+    assert L.moeq_route_workspace_size(16, 8, 2, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def _desc(E=2, H=256, I=512, G=64, fmt=0, bits=4, r=0):
+    from bit_quantized_moe_token_amd import _lib
+    nb = 3 * E
+    keep = []
+    bits_arr = (ctypes.c_uint8 * nb)(*([bits] * nb))
+    ptrs = (ctypes.c_void_p * nb)(*([4096] * nb))
+    keep += [bits_arr, ptrs]
+    vpp = lambda a: ctypes.cast(a, _lib.c_vpp)
+    d = _lib.LayerDesc(E, H, I, G, fmt, ctypes.cast(bits_arr, _lib.c_u8p), vpp(ptrs), vpp(ptrs),
+                       vpp(ptrs), vpp(ptrs), r, vpp(ptrs) if r else None, vpp(ptrs) if r else None,
+                       0, 0, None, None)
+    return d, keep
+
+
+def test_pack_size_and_validation(L):
+    d, keep = _desc()
+    n = ctypes.c_size_t(0)
+    assert L.moeq_pack_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # codes 4 bit + fp16 scale + u8 zero per 64-group, three blocks, two experts
+    assert n.value >= 2 * 3 * (256 * 512 // 2 + 256 * 512 // 64 * 3)
+    bad, keep2 = _desc(H=200)
+    assert L.moeq_pack_size(ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad, keep3 = _desc(G=32)
+    assert L.moeq_pack_size(ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad, keep4 = _desc(bits=5)
+    assert L.moeq_pack_size(ctypes.byref(bad), ctypes.byref(n)) == 1
+    bad, keep5 = _desc(r=12)
+    assert L.moeq_pack_size(ctypes.byref(bad), ctypes.byref(n)) == 1
+    bad, keep6 = _desc(fmt=1, G=64)
+    assert L.moeq_pack_size(ctypes.byref(bad), ctypes.byref(n)) == 2
+    # a too-small buffer is rejected before anything is enqueued
+    h = ctypes.c_void_p(0)
+    assert L.moeq_pack(ctypes.byref(d), ctypes.c_void_p(4096), 256, None, ctypes.byref(h)) == 3
+    assert L.moeq_pack(ctypes.byref(d), ctypes.c_void_p(4097), 1 << 40, None, ctypes.byref(h)) == 1
+
+
+def test_ffn_validation(L):
+    from bit_quantized_moe_token_amd import _lib
+    r = _lib.Routing(16, 16, 16, 16, 16)
+    assert L.moeq_expert_ffn(None, None, 4, 2, ctypes.byref(r), 0, None, 0, None, 0, None, None) == 1
+    n = ctypes.c_size_t(0)
+    assert L.moeq_ffn_workspace_size(None, 4, 2, None, ctypes.byref(n)) == 1
+    assert L.moeq_debug_unpack(None, 0, 0, None, None) == 1

@@ -1,0 +1,117 @@
+"""GPU parity of the routed expert layer against the fp64 oracle on the five
+seeded workloads (reduced dimensions where the oracle would be slow, with
+the same structure), plus compensation switches, determinism and token
+permutation."""
+
+import numpy as np
+import pytest
+
+from synth import configs, gen
+from tests import layers
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# (config, overrides) — reduced Mixtral layers keep H, I multiples of 128
+# with a ragged tile tail (1792 / 128 = 14 tiles); T keeps the regime
+CASES = {
+    "tiny": ("tiny", {}),
+    "decode": ("decode", dict(H=512, I=1792)),
+    "prefill": ("prefill", dict(H=512, I=1792, T=1024)),
+    "finegrained": ("finegrained", {}),
+    "bitplane": ("bitplane", dict(E=32, T=128)),
+}
+
+_cache = {}
+
+
+def _setup(case, seed=0):
+    key = (case, seed)
+    if key not in _cache:
+        name, over = CASES[case]
+        cfg = configs.reduced(configs.get(name), **over) if over else configs.get(name)
+        orc = layers.oracle_layer(cfg, seed, cache_blocks=3 * cfg["E"])
+        dev = layers.device_layer(cfg, seed, orc)
+        x = gen.gen_x(cfg, seed)
+        logits = gen.gen_logits(cfg, seed)
+        _cache.clear()
+        _cache[key] = (cfg, orc, dev, x, logits)
+    return _cache[key]
+
+
+def _run(dev, cfg, x, logits, n_comp, out_dtype=torch.float16, split_k=0):
+    from bit_quantized_moe_token_amd import moeq
+    xd = torch.from_numpy(x).cuda()
+    rt = moeq.route(torch.from_numpy(logits).cuda(), cfg["k"])
+    y = moeq.expert_ffn(dev, xd, rt, n_comp, out_dtype=out_dtype, split_k=split_k)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_ffn_matches_oracle(case):
+    cfg, orc, dev, x, logits = _setup(case)
+    y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
+    rel, fro = layers.check_y(y.cpu().numpy(), ref, case)
+    print(f"{case}: max|err|/rms {rel:.2e}  fro {fro:.2e}")
+    # fp16 output stays inside the same bound
+    y16 = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float16)
+    layers.check_y(y16.float().cpu().numpy(), ref, case + " fp16")
+
+
+@pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane"])
+def test_ffn_compensation_switch(case):
+    """n_comp in {0, 1, k} against the oracle; n_comp = 0 equals the layer
+    without factors bit for bit."""
+    cfg, orc, dev, x, logits = _setup(case)
+    k = cfg["k"]
+    for n_comp in (0, 1, k):
+        y = _run(dev, cfg, x, logits, n_comp, out_dtype=torch.float32)
+        layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, n_comp), f"{case} n_comp={n_comp}")
+
+
+def test_rank0_bitwise_equals_uncompensated():
+    from bit_quantized_moe_token_amd import moeq
+    cfg, orc, dev, x, logits = _setup("tiny")
+    y0 = _run(dev, cfg, x, logits, 0, out_dtype=torch.float32)
+    # the same codes packed without any factors
+    E = cfg["E"]
+    bits = gen.gen_bits(cfg, 0)
+    blocks = [moeq.quantize_block(torch.from_numpy(gen.gen_weight_block(cfg, 0, e, b)).cuda(),
+                                  "int", int(bits[e, b]), cfg["G"]) for e in range(E) for b in range(3)]
+    plain = moeq.PackedLayer(E, cfg["H"], cfg["I"], cfg["G"], "int", bits, blocks)
+    y1 = _run(plain, cfg, x, logits, cfg["k"], out_dtype=torch.float32)
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("case", ["decode", "finegrained"])
+def test_ffn_deterministic_and_split_invariant(case):
+    cfg, orc, dev, x, logits = _setup(case)
+    a = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    b = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
+    for s in (1, 2, 3):
+        c = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, split_k=s)
+        layers.check_y(c.cpu().numpy(), ref, f"{case} split_k={s}")
+
+
+@pytest.mark.parametrize("case", ["tiny", "finegrained"])
+def test_ffn_token_permutation(case):
+    """Permuting tokens (and their logits) permutes the output exactly."""
+    cfg, orc, dev, x, logits = _setup(case)
+    perm = np.random.default_rng(5).permutation(cfg["T"])
+    y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    yp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32)
+    assert torch.equal(yp, y[torch.from_numpy(perm).cuda()])
+
+
+def test_ffn_zero_input_and_few_tokens():
+    cfg, orc, dev, x, logits = _setup("tiny")
+    y = _run(dev, cfg, np.zeros_like(x), logits, cfg["k"], out_dtype=torch.float32)
+    assert torch.count_nonzero(y) == 0
+    for T in (1, 3, 17):
+        sub = dict(cfg, T=T)
+        y = _run(dev, sub, x[:T].copy(), logits[:T].copy(), cfg["k"], out_dtype=torch.float32)
+        layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, sub, x[:T], logits[:T], cfg["k"]), f"T={T}")

@@ -1,0 +1,58 @@
+"""GPU parity of routing and the counting sort: ids, offsets, sorted pairs and
+their inverse bit-exact against the oracle; gates within 2e-6."""
+
+import numpy as np
+import pytest
+
+from oracle import forward
+from synth import configs, gen
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _route(logits, k):
+    from bit_quantized_moe_token_amd import moeq
+    rt = moeq.route(torch.from_numpy(logits).cuda(), k)
+    torch.cuda.synchronize()
+    return rt
+
+
+def _check(logits, k):
+    rt = _route(logits, k)
+    ref = forward.route(logits, k)
+    T = logits.shape[0]
+    assert np.array_equal(rt.offsets.cpu().numpy(), ref["offsets"])
+    if T == 0:
+        return
+    assert np.array_equal(rt.ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(rt.sorted_pairs.cpu().numpy(), ref["sorted_pairs"])
+    assert np.array_equal(rt.pair_pos.cpu().numpy(), ref["pair_pos"])
+    g = rt.gates.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - ref["gates"])) <= 2e-6
+    assert np.max(np.abs(g.sum(1) - 1)) <= 2e-6
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "finegrained", "bitplane"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_route_configs(name, seed):
+    cfg = configs.get(name)
+    _check(gen.gen_logits(cfg, seed), cfg["k"])
+
+
+@pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 8), (5, 3, 1), (333, 256, 7), (70, 64, 64),
+                                   (2000, 5, 2), (1030, 128, 8), (4096, 2, 2)])
+def test_route_shapes_and_ties(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = (rng.integers(-2, 3, size=(T, E)) * 0.25).astype(np.float32)   # many ties
+    _check(logits, k)
+    _check(rng.standard_normal((T, E)).astype(np.float32), k)
+
+
+def test_route_deterministic():
+    cfg = configs.get("prefill")
+    logits = gen.gen_logits(cfg, 0)
+    a = _route(logits, 2)
+    b = _route(logits, 2)
+    for f in ("ids", "gates", "offsets", "sorted_pairs", "pair_pos"):
+        assert torch.equal(getattr(a, f), getattr(b, f))
