@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed low-bit MoE expert layer on one MI355X.
+
+One step = one pass of the hot path over one batch: moeq_route (top-k +
+counting sort) followed by moeq_expert_ffn (V-projections, gate/up + SwiGLU,
+down, combine) on a seeded synthetic layer.  Default workload: the
+Mixtral-shaped decode layer (8 experts, top-2, H 4096, I 14336, 16 tokens,
+int3 group-128 codes, rank-32 compensators).  Inputs are resident in HBM
+before timing; weights rotate over several packed copies so that no step
+finds them in the 256 MB last-level cache.
+
+Prints one JSON line (see the repository's design notes for every field).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "expert-FFN tokens/s; decode HBM GB/s and prefill TFLOP/s as % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA peak, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["ffn.hip", "decode.hpp", "layer.hpp", "common.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_moe_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", choices=["decode", "prefill", "finegrained", "bitplane", "tiny"],
+                   default="decode")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--path", type=int, default=0, help="moeq_path (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (reference kernel for counter scaling)")
+    p.add_argument("--no-extra", action="store_true", help="skip the extra prefill measurement")
+    return p.parse_args()
+
+
+def build_layers(cfg, seed, copies, formats):
+    """Quantize the seeded fp16 weights on the device and pack `copies`
+    copies per requested (fmt, bits) variant.  Returns {name: [layers]}."""
+    import numpy as np
+    import torch
+    from bit_quantized_moe_token_amd import moeq
+    from synth import gen
+
+    E = cfg["E"]
+    blocks = {name: [] for name in formats}
+    bits_of = {}
+    for name, c in formats.items():
+        bits_of[name] = gen.gen_bits(c, seed)
+    factors = []
+    for e in range(E):
+        for blk in range(3):
+            W = torch.from_numpy(gen.gen_weight_block(cfg, seed, e, blk)).cuda()
+            for name, c in formats.items():
+                blocks[name].append(moeq.quantize_block(W, c["fmt"], int(bits_of[name][e, blk]), c["G"]))
+            del W
+            if cfg["r"]:
+                f = gen.gen_factors(cfg, seed, e, blk)
+                factors.append((torch.from_numpy(f[0]).cuda(), torch.from_numpy(f[1]).cuda()))
+    shared = None
+    if cfg.get("rs"):
+        shared = []
+        for g in range(gen.n_groups(cfg)):
+            for blk in range(3):
+                f = gen.gen_shared_factors(cfg, seed, g, blk)
+                shared.append((torch.from_numpy(f[0]).cuda(), torch.from_numpy(f[1]).cuda()))
+    out = {}
+    for name, c in formats.items():
+        out[name] = [moeq.PackedLayer(E, cfg["H"], cfg["I"], c["G"], c["fmt"], bits_of[name],
+                                      blocks[name], factors if cfg["r"] else None, shared,
+                                      cfg.get("share", 0))
+                     for _ in range(copies[name])]
+    torch.cuda.synchronize()
+    del blocks
+    return out
+
+
+def algorithmic(cfg, layer, offsets, sorted_pairs, n_comp):
+    """Algorithmic bytes and flops of one call from the actual routing:
+    per active expert its codes (b bits/weight or top-q planes), fp16 scale
+    + 1 B zero per (row, group) or its LUT, fp16 factors of blocks with a
+    compensated pair (shared factors once per active group); x and y fp16.
+    Flops: 2 m N K per block plus 2 r (N + K) per compensated pair and block.
+    Also the bytes of the gate/up kernel alone (codes, metadata and U of the
+    gate and up blocks, x read, h written)."""
+    import numpy as np
+    E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
+    r, rs = cfg["r"], cfg.get("rs", 0)
+    counts = np.diff(offsets)
+    comp_cnt = np.zeros(E, dtype=np.int64)
+    for pos in range(len(sorted_pairs)):
+        e = int(np.searchsorted(offsets, pos, side="right") - 1)
+        if int(sorted_pairs[pos]) % k < n_comp:
+            comp_cnt[e] += 1
+    total, flops, gu = 0, 0.0, 0
+    groups = set()
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        for blk in range(3):
+            N, K = (I, H) if blk < 2 else (H, I)
+            b = layer.block_bytes(e, blk)          # codes + metadata + U, V
+            fac = (N + K) * r * 2
+            body = b - fac
+            total += body + (fac if comp_cnt[e] else 0)
+            flops += 2.0 * counts[e] * N * K + 2.0 * (r + rs) * (N + K) * comp_cnt[e]
+            if blk < 2:
+                gu += body + (N * r * 2 if comp_cnt[e] else 0)
+        if rs and comp_cnt[e]:
+            groups.add(e // cfg["share"])
+    for g in groups:
+        for blk in range(3):
+            total += layer.shared_bytes(g, blk)
+            if blk < 2:
+                N = I
+                gu += N * rs * 2
+    P = T * k
+    total += 2 * T * H * 2
+    gu += T * H * 2 + P * I * 2
+    return dict(bytes=int(total), flops=float(flops), gateup_bytes=int(gu),
+                active=int((counts > 0).sum()), counts=[int(c) for c in counts])
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True):
+    import numpy as np
+    import torch
+    from bit_quantized_moe_token_amd import moeq
+    from synth import gen
+
+    T, k = cfg["T"], cfg["k"]
+    x = torch.from_numpy(gen.gen_x(cfg, seed)).cuda()
+    logits = torch.from_numpy(gen.gen_logits(cfg, seed)).cuda()
+    rt = moeq.RoutingOut(T, cfg["E"], k, x.device)
+    y = torch.empty((T, cfg["H"]), dtype=torch.float16, device=x.device)
+    ws = moeq.FfnWorkspace(layers_list[0], T, k, path)
+    R = len(layers_list)
+
+    def step(i):
+        moeq.route(logits, k, out=rt)
+        moeq.expert_ffn(layers_list[i % R], x, rt, cfg["n_comp"], out=y, ws=ws, path=path)
+
+    ms = time_steps(step, steps, warmup)
+    prof = {}
+    if profile:
+        moeq.profile_enable(True)
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        prof = moeq.profile_read()
+        moeq.profile_enable(False)
+    torch.cuda.synchronize()
+    offsets = rt.offsets.cpu().numpy()
+    sp = rt.sorted_pairs.cpu().numpy()
+    alg = algorithmic(cfg, layers_list[0], offsets, sp, cfg["n_comp"])
+    return ms, prof, alg
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, 5 times (reference for counter scaling)."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(cfg, seed, sample_tokens):
+    """The oracle as it stands on a bounded sample of the same workload:
+    route all tokens, then the full expert FFN and combine for the sampled
+    tokens (PTQ of the needed blocks done before timing)."""
+    import numpy as np
+    from oracle import forward
+    from oracle.layer import OracleLayer
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    E, k = cfg["E"], cfg["k"]
+    bits = gen.gen_bits(cfg, seed)
+
+    def rows(e, blk, r):
+        return gen.gen_weight_block(cfg, seed, e, blk) if r is None else gen.gen_weight_rows(cfg, seed, e, blk, r)
+
+    fac = (lambda e, blk: gen.gen_factors(cfg, seed, e, blk)) if cfg["r"] else None
+    sh = (lambda g, blk: gen.gen_shared_factors(cfg, seed, g, blk)) if cfg.get("rs") else None
+    x = gen.gen_x(cfg, seed)
+    logits = gen.gen_logits(cfg, seed)
+    ids = forward.topk_ids(logits, k)
+    tokens = list(range(sample_tokens))
+    experts = sorted({int(e) for t in tokens for e in ids[t]})
+    orc = OracleLayer(E, cfg["H"], cfg["I"], cfg["G"], cfg["fmt"], bits, rows, factors=fac,
+                      shared=sh, share=cfg.get("share", 0), cache_blocks=3 * len(experts) + 3)
+    for e in experts:                      # PTQ (data preparation) outside the timing
+        for blk in range(3):
+            orc.qblock(e, blk)
+    t0 = time.perf_counter()
+    forward.moe_forward(orc, x, logits, k, cfg["n_comp"], tokens=np.array(tokens))
+    dt = time.perf_counter() - t0
+    return dict(value=len(tokens) / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{len(tokens)} of {cfg['T']} tokens of the same layer: routing of all tokens, "
+                       f"fp64 dequantization of the {len(experts)} experts they use, compensated SwiGLU "
+                       f"FFN and combine ({dt:.1f} s)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the expert layer is not "
+              "sharded in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = configs.get(args.workload)
+    t_setup = time.time()
+    formats = {"main": cfg}
+    copies = {"main": 3 if cfg["H"] * cfg["I"] * cfg["E"] > 1e8 else 2}
+    extra_cfg = None
+    if args.workload == "decode" and not args.no_extra:
+        # the same Mixtral-shaped weights, int4, in the prefill regime
+        extra_cfg = configs.get("prefill")
+        formats["prefill"] = extra_cfg
+        copies["prefill"] = 1
+    layers = build_layers(cfg, args.seed, copies, formats)
+    setup_s = time.time() - t_setup
+    if args.copy_calibration:
+        copy_calibration()
+
+    ms, prof, alg = run_workload(cfg, layers["main"], args.seed, args.steps, args.warmup, args.path)
+    T = cfg["T"]
+    tokens_s = T / (ms * 1e-3)
+
+    kern = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in prof.items()}
+    gu = kern.get("gateup_stream", {}).get("avg_us")
+    achieved = alg["gateup_bytes"] / (gu * 1e-6) / 1e9 if gu else None
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        ent = tr.get(cfg["name"], {})
+        if ent.get("source_hash") == kernel_source_hash():
+            traffic = ent.get("gateup_stream_bytes")
+    roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=(achieved / HBM_PEAK_GBS) if achieved else None, traffic=traffic,
+                    kernel="gateup_stream", bytes_per_launch=alg["gateup_bytes"])
+    ffn_us = sum(v["avg_us"] for n, v in kern.items() if n != "route")
+    out = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "T": T, "E": cfg["E"], "k": cfg["k"], "H": cfg["H"],
+                   "I": cfg["I"], "fmt": cfg["fmt"], "bits": cfg["bits"], "G": cfg["G"],
+                   "r": cfg["r"], "n_comp": cfg["n_comp"], "seed": args.seed,
+                   "weight_copies": copies["main"], "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "layer": dict(alg_bytes=alg["bytes"], alg_flops=alg["flops"], active_experts=alg["active"],
+                      expert_counts=alg["counts"],
+                      hbm_frac_step=alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      hbm_frac_kernels=(alg["bytes"] / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS) if ffn_us else None),
+        "kernels": kern,
+        "setup_s": setup_s,
+    }
+    if extra_cfg is not None:
+        pms, pprof, palg = run_workload(extra_cfg, layers["prefill"], args.seed, max(3, args.steps // 20),
+                                        max(1, args.warmup // 10), args.path)
+        pk = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in pprof.items()}
+        out["prefill"] = dict(workload=extra_cfg["name"], ms_per_step=pms,
+                              tokens_s=extra_cfg["T"] / (pms * 1e-3), alg_flops=palg["flops"],
+                              tflops=palg["flops"] / (pms * 1e-3) / 1e12,
+                              mfma_frac=palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                              expert_counts=palg["counts"], kernels=pk)
+    del layers
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.seed, 2 if cfg["H"] >= 4096 else 4)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

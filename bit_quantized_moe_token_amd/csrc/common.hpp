@@ -57,6 +57,14 @@ void prof_end(const char *name, hipStream_t s);
 
 // ------------------------------------------------------ device helpers --
 
+// Loads through the global address space (the pointers handed to kernels
+// are generic; telling the compiler lets it use global_load and the vector
+// memory counter only).
+template <typename T>
+__device__ __forceinline__ T gld(const void *p) {
+  return *(const __attribute__((address_space(1))) T *)(p);
+}
+
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return (a & m) | c;   // v_and_or_b32
 }

@@ -1,0 +1,93 @@
+// Shared declarations of the expert-FFN kernels (device helpers, argument
+// block and host-side launchers).
+#pragma once
+#include <algorithm>
+#include "common.hpp"
+
+namespace moeq {
+
+constexpr int kMT = 64;            // tokens per chunk (up to four 16-row MFMA tiles)
+constexpr int kStripsPerWG = 4;    // one 16-row strip per wave
+
+struct FfnArgs {
+  const BlockDesc *desc;
+  const int32_t *offsets;
+  const int32_t *sorted_pairs;
+  const uint16_t *x;
+  const float *gates;
+  const int32_t *pair_pos;
+  int E, H, I, k, T, n_comp;
+  int r, rs, Rp, Rsp, RZ;
+  int comp_on;
+  int G, fmt;
+  uint16_t *z_gu;   // [P][2][RZ] fp16
+  uint16_t *z_d;    // [P][RZ] fp16
+  uint16_t *h;      // [P][I] fp16
+  float *ypart;     // [splits][P][H] fp32
+  int splits;
+  int P;
+  int nsub_max;     // largest number of 16-token tiles a chunk can have
+};
+
+struct Chunk {
+  int e, m0, cnt, base;
+};
+
+// Chunk c of the expert-major chunk list (each expert's tokens cut into
+// pieces of kMT): expert, first token within the expert, token count and
+// first sorted position.  Wave-uniform; false when c is past the end.
+__device__ __forceinline__ bool find_chunk(const int32_t *__restrict__ off, int E, int c, Chunk *out) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int b = 0; b < E; b += kWave) {
+    const int e = b + lane;
+    const int cnt = e < E ? off[e + 1] - off[e] : 0;
+    const int nc = (cnt + kMT - 1) / kMT;
+    int incl = nc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += t;
+    }
+    const int excl = carry + incl - nc;
+    const uint64_t hit = __ballot(c >= excl && c < excl + nc);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int ex = __shfl(excl, src, kWave);
+      const int cn = __shfl(cnt, src, kWave);
+      out->e = b + src;
+      out->m0 = (c - ex) * kMT;
+      out->cnt = std::min(kMT, cn - out->m0);
+      out->base = off[out->e] + out->m0;
+      return true;
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  return false;
+}
+
+__device__ __forceinline__ f16x8 load_a(const uint16_t *p) {
+  return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ f16x8 pack_b(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// Upper bound of the number of chunks for T tokens, top-k, E experts.
+inline int max_chunks(int E, int T, int k) {
+  const int64_t P = (int64_t)T * k;
+  const int64_t a = (int64_t)E * ((T + kMT - 1) / kMT);
+  const int64_t act = std::min<int64_t>(E, P);
+  const int64_t b = (P + act * (kMT - 1)) / kMT;
+  return (int)std::max<int64_t>(0, std::min(a, b));
+}
+
+// Launchers (stream.hip, lowrank.hip).
+void launch_gateup_stream(const FfnArgs &a, int grid, hipStream_t s);
+void launch_down_stream(const FfnArgs &a, int grid, hipStream_t s);
+void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s);
+void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s);
+
+}  // namespace moeq

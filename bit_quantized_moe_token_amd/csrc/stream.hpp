@@ -1,0 +1,535 @@
+// Weight-streaming expert GEMMs: gate/up (+ low-rank epilogue + SwiGLU) and
+// down (+ low-rank epilogue, split-K).  PagedWeight review summary: one
+// fused kernel executes the per-block variable bitwidths; MxMoE abstract:
+// per-linear-block bitwidths and uneven tokens per expert; TileQ abstract:
+// the low-rank terms fused into the expert pass.
+//
+// A workgroup = 4 waves = 4 strips of 16 output rows of one expert, for one
+// chunk of up to 64 of the expert's tokens (NSUB 16-row MFMA tiles).  Every
+// packed weight is read from HBM exactly once per chunk.  K is walked in
+// groups of four 128-column tiles:
+//   - the group's activations (NSUB*16 rows x 512 columns, rows gathered by
+//     token) sit in LDS, row stride padded by 16 B so that the MFMA A reads
+//     are bank-conflict free;
+//   - each wave loads the group's packed codes (128-bit loads) and metadata
+//     into registers, then the next group's activations (so that waiting
+//     for the codes never waits for them); several resident workgroups per
+//     SIMD cover the HBM latency;
+//   - the group is decoded in registers and fed to v_mfma_f32_16x16x32_f16
+//     (B = decoded weights, A = activations from LDS).  INT blocks produce
+//     exact (c - z) operands and apply the fp16 scale to each quantization
+//     group's fp32 sum; bit-plane blocks look their q-bit indices up in
+//     per-row LUTs staged in LDS.
+// Bitwidths are template parameters: the kernel entry dispatches on the
+// (gate, up) or down bitwidths of the chunk's expert.
+#pragma once
+#include "common.hpp"
+#include "decode.hpp"
+#include "ffn.hpp"
+#include "layer.hpp"
+
+namespace moeq {
+
+constexpr int kXStride = 4 * kTileK + 8;   // halves per staged activation row
+constexpr int kLutBlk = 4 * 16 * 16;       // halves of one block's staged LUTs (4 tiles x 16 rows x 16)
+
+// Packed data of one strip of one block for one group of C tiles.
+template <int B, bool PLANE>
+struct Group {
+  static constexpr int NW = PLANE ? 4 * B : 4 * B;   // INT: 4 tiles x B dwords; planes: B planes x 4 tiles
+  uint32_t w[NW];
+  uint32_t sc[4];   // INT: fp16 scale of (tile t, group gi) at half t*GPT+gi
+  uint32_t zz[2];   // INT: zero of (tile t, group gi) at byte t*GPT+gi
+};
+
+template <int B, int C, int GPT>
+__device__ __forceinline__ void load_int_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, false> &g) {
+  const int lane = threadIdx.x & 63, r = lane & 15;
+  const uint8_t *p = d.codes + code_offset(strip, 4 * g4, lane, n_kt, 4 * B);
+  if (C == 4) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const u32x4 v = gld<u32x4>(p + 16 * i);
+      g.w[4 * i] = v[0]; g.w[4 * i + 1] = v[1]; g.w[4 * i + 2] = v[2]; g.w[4 * i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C * B; ++i) g.w[i] = gld<uint32_t>(p + 4 * i);
+  }
+  const uint64_t mi = meta_index(strip, 4 * g4, r, 0, n_kt, GPT);
+  const uint16_t *sp = d.scales + mi;
+  const uint8_t *zp = d.zeros + mi;
+  if (C == 4 && GPT == 1) {
+    const u32x2 v = gld<u32x2>(sp);
+    g.sc[0] = v[0]; g.sc[1] = v[1];
+    g.zz[0] = gld<uint32_t>(zp);
+  } else if (C == 4 && GPT == 2) {
+    const u32x4 v = gld<u32x4>(sp);
+    g.sc[0] = v[0]; g.sc[1] = v[1]; g.sc[2] = v[2]; g.sc[3] = v[3];
+    const u32x2 z = gld<u32x2>(zp);
+    g.zz[0] = z[0]; g.zz[1] = z[1];
+  } else {
+    g.sc[0] = g.sc[1] = g.sc[2] = g.sc[3] = 0;
+    g.zz[0] = g.zz[1] = 0;
+#pragma unroll
+    for (int q = 0; q < C * GPT; ++q) {
+      g.sc[q >> 1] |= (uint32_t)gld<uint16_t>(sp + q) << (16 * (q & 1));
+      g.zz[q >> 2] |= (uint32_t)gld<uint8_t>(zp + q) << (8 * (q & 3));
+    }
+  }
+}
+
+template <int Q, int C>
+__device__ __forceinline__ void load_plane_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<Q, true> &g) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t off = code_offset(strip, 4 * g4, lane, n_kt, 4);
+#pragma unroll
+  for (int u = 0; u < Q; ++u) {
+    const uint8_t *p = d.codes + u * d.plane_bytes + off;
+    if (C == 4) {
+      const u32x4 v = gld<u32x4>(p);
+      g.w[4 * u] = v[0]; g.w[4 * u + 1] = v[1]; g.w[4 * u + 2] = v[2]; g.w[4 * u + 3] = v[3];
+    } else {
+#pragma unroll
+      for (int t = 0; t < C; ++t) g.w[4 * u + t] = gld<uint32_t>(p + 4 * t);
+    }
+  }
+}
+
+template <int B, bool PLANE, int C, int GPT>
+__device__ __forceinline__ void load_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, PLANE> &g) {
+  if constexpr (PLANE) load_plane_group<B, C>(d, strip, g4, n_kt, g);
+  else load_int_group<B, C, GPT>(d, strip, g4, n_kt, g);
+}
+
+// A operand of token tile s, tile tl, step j from the staged activations.
+__device__ __forceinline__ f16x8 lds_a(const uint16_t *xs, int s, int tl, int j) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const f16x8 *>(xs + (16 * s + (lane & 15)) * kXStride + tl * kTileK +
+                                          32 * j + 8 * (lane >> 4));
+}
+
+// Decoded B operand of step j of tile tl (INT: exact (c - z) pairs).
+template <int B>
+__device__ __forceinline__ f16x8 int_bop(const uint32_t *dw, int j, const PairConst *pc) {
+  return pack_b(int_pair_cz<B>(dw, 4 * j + 0, pc), int_pair_cz<B>(dw, 4 * j + 1, pc),
+                int_pair_cz<B>(dw, 4 * j + 2, pc), int_pair_cz<B>(dw, 4 * j + 3, pc));
+}
+
+__device__ __forceinline__ float int_zero(const uint32_t *zz, int q) {
+  return (float)((zz[q >> 2] >> (8 * (q & 3))) & 0xffu);
+}
+__device__ __forceinline__ float int_scale(const uint32_t *sc, int q) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)(sc[q >> 1] >> (16 * (q & 1))));
+}
+
+// One group of C tiles for NB INT blocks sharing the A operands: each
+// activation fragment read from LDS feeds the MFMAs of every block before
+// the next is read.  Per quantization group: fp32 partial sums of
+// (c - z) * x, then acc += scale * partial.
+template <int NSUB, int NB, int B0, int B1, int C, int GPT>
+__device__ __forceinline__ void compute_int(const Group<B0, false> &g0, const Group<B1, false> &g1,
+                                            const uint16_t *xs, f32x4 (*acc)[NSUB]) {
+#pragma unroll
+  for (int tl = 0; tl < C; ++tl) {
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int q = tl * GPT + gi;
+      PairConst pc0[9], pc1[9];
+      fill_pair_consts<B0>(pc0, int_zero(g0.zz, q));
+      if (NB == 2) fill_pair_consts<B1>(pc1, int_zero(g1.zz, q));
+      f32x4 p0[NSUB], p1[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) { p0[s] = f32x4{0.f, 0.f, 0.f, 0.f}; p1[s] = p0[s]; }
+#pragma unroll
+      for (int jj = 0; jj < 4 / GPT; ++jj) {
+        const int j = gi * (4 / GPT) + jj;
+        const f16x8 b0 = int_bop<B0>(g0.w + tl * B0, j, pc0);
+        f16x8 b1;
+        if (NB == 2) b1 = int_bop<B1>(g1.w + tl * B1, j, pc1);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const f16x8 av = lds_a(xs, s, tl, j);
+          p0[s] = mfma16(av, b0, p0[s]);
+          if (NB == 2) p1[s] = mfma16(av, b1, p1[s]);
+        }
+      }
+      const float s0 = int_scale(g0.sc, q);
+      const float s1 = NB == 2 ? int_scale(g1.sc, q) : 0.f;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[0][s][i] = __builtin_fmaf(s0, p0[s][i], acc[0][s][i]);
+          if (NB == 2) acc[1][s][i] = __builtin_fmaf(s1, p1[s][i], acc[1][s][i]);
+        }
+      }
+    }
+  }
+}
+
+// Decoded B operand of step j from the merged bit-plane indices and the
+// lane's row LUT.
+template <int Q>
+__device__ __forceinline__ f16x8 plane_bop(const uint32_t *tp, int j, const uint32_t *L) {
+  const uint32_t m = plane_merge<Q>(tp, j);
+  return pack_b(lut_pair<Q>(m & 0x000F000Fu, L), lut_pair<Q>((m >> 4) & 0x000F000Fu, L),
+                lut_pair<Q>((m >> 8) & 0x000F000Fu, L), lut_pair<Q>((m >> 12) & 0x000F000Fu, L));
+}
+
+template <int Q>
+__device__ __forceinline__ void lut_row(const uint16_t *lut, int tl, uint32_t *L) {
+  constexpr int NQ = 1 << Q;
+  const int lane = threadIdx.x & 63;
+  const uint32_t *lp = reinterpret_cast<const uint32_t *>(lut + (tl * 16 + (lane & 15)) * NQ);
+#pragma unroll
+  for (int i = 0; i < NQ / 2; ++i) L[i] = lp[i];
+}
+
+template <int NSUB, int NB, int Q0, int Q1, int C>
+__device__ __forceinline__ void compute_plane(const Group<Q0, true> &g0, const Group<Q1, true> &g1,
+                                              const uint16_t *xs, const uint16_t *lut, f32x4 (*acc)[NSUB]) {
+#pragma unroll
+  for (int tl = 0; tl < C; ++tl) {
+    uint32_t L0[1 << (Q0 - 1)], L1[1 << (Q1 - 1)];
+    lut_row<Q0>(lut, tl, L0);
+    if (NB == 2) lut_row<Q1>(lut + kLutBlk, tl, L1);
+    uint32_t t0[Q0], t1[Q1];
+#pragma unroll
+    for (int u = 0; u < Q0; ++u) t0[u] = g0.w[4 * u + tl];
+#pragma unroll
+    for (int u = 0; u < Q1; ++u) t1[u] = NB == 2 ? g1.w[4 * u + tl] : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 b0 = plane_bop<Q0>(t0, j, L0);
+      f16x8 b1;
+      if (NB == 2) b1 = plane_bop<Q1>(t1, j, L1);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const f16x8 av = lds_a(xs, s, tl, j);
+        acc[0][s] = mfma16(av, b0, acc[0][s]);
+        if (NB == 2) acc[1][s] = mfma16(av, b1, acc[1][s]);
+      }
+    }
+  }
+}
+
+// ---- activation staging: NSUB*16 rows x 512 columns of group g4.  Pass p
+// of NSUB*4 loads row 4p + wave (wave-uniform row pointer), lane = 16 B.
+template <int NSUB>
+struct XStage {
+  u32x4 v[NSUB * 4];
+};
+
+template <int NSUB>
+__device__ __forceinline__ void stage_load(XStage<NSUB> &st, const uint16_t *const *rowp, int g4, int c) {
+  const int lane = threadIdx.x & 63;
+  const int col = 4 * kTileK * g4 + 8 * lane;      // halves
+#pragma unroll
+  for (int p = 0; p < NSUB * 4; ++p) {
+    if (lane < 16 * c) st.v[p] = gld<u32x4>(rowp[p] + col);
+  }
+}
+
+template <int NSUB>
+__device__ __forceinline__ void stage_store(const XStage<NSUB> &st, uint16_t *xs, int c) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < NSUB * 4; ++p) {
+    if (lane < 16 * c) *reinterpret_cast<u32x4 *>(xs + (4 * p + wave) * kXStride + 8 * lane) = st.v[p];
+  }
+}
+
+// LUT staging of one wave's strip for a group: 4 tiles x 16 rows x NQ
+// halves, contiguous in the packed LUT; lane l holds 2*NQ bytes.
+template <int Q>
+struct LutStage {
+  uint32_t v[1 << (Q - 1)];
+};
+
+template <int Q>
+__device__ __forceinline__ void lut_load(const BlockDesc &d, int strip, int g4, int n_kt, int c, LutStage<Q> &ls) {
+  constexpr int NQ = 1 << Q;
+  const int lane = threadIdx.x & 63;
+  const uint16_t *p = d.lut + lut_index(strip, 4 * g4, 0, 0, n_kt, NQ) + lane * NQ;
+  if (lane < 16 * c) {
+#pragma unroll
+    for (int i = 0; i < NQ / 2; ++i) ls.v[i] = gld<uint32_t>(p + 2 * i);
+  }
+}
+
+template <int Q>
+__device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, int c) {
+  constexpr int NQ = 1 << Q;
+  const int lane = threadIdx.x & 63;
+  if (lane < 16 * c) {
+#pragma unroll
+    for (int i = 0; i < NQ / 2; ++i) reinterpret_cast<uint32_t *>(dst + lane * NQ)[i] = ls.v[i];
+  }
+}
+
+// Low-rank epilogue: acc += U z for one factor set (z fp16 rows of the
+// chunk's pairs; zero rows for uncompensated pairs and columns >= R).
+template <int NSUB>
+__device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, int row,
+                                            const uint16_t *zbase, int zstride, const Chunk &ch,
+                                            f32x4 *acc) {
+  const int lane = threadIdx.x & 63, kq = lane >> 4;
+  for (int ks = 0; ks < Rpad / 32; ++ks) {
+    const int col = 32 * ks + 8 * kq;
+    f16x8 bop = pack_b(0, 0, 0, 0);
+    if (col < R) bop = load_a(U + (int64_t)row * R + col);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int m = std::min(16 * s + (lane & 15), ch.cnt - 1);
+      acc[s] = mfma16(load_a(zbase + (int64_t)(ch.base + m) * zstride + col), bop, acc[s]);
+    }
+  }
+}
+
+// Stage group g's activations (and bit-plane LUTs) into LDS: load, then
+// (after the caller's barrier) store.
+template <int NSUB, bool PLANE, int B0, int B1, int NB>
+struct Stager {
+  XStage<NSUB> st;
+  LutStage<B0> l0;
+  LutStage<B1> l1;
+  __device__ __forceinline__ void load(const BlockDesc *dsc, const uint16_t *const *rowp, int strip, int g4,
+                                       int n_kt, int c) {
+    stage_load<NSUB>(st, rowp, g4, c);
+    if constexpr (PLANE) {
+      lut_load<B0>(dsc[0], strip, g4, n_kt, c, l0);
+      if constexpr (NB == 2) lut_load<B1>(dsc[1], strip, g4, n_kt, c, l1);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t *xs, uint16_t *lut_lds, int c) {
+    stage_store<NSUB>(st, xs, c);
+    if constexpr (PLANE) {
+      lut_store<B0>(l0, lut_lds, c);
+      if constexpr (NB == 2) lut_store<B1>(l1, lut_lds + kLutBlk, c);
+    }
+  }
+};
+
+// One group of C tiles for the NB blocks (bitwidths B0, B1).
+template <int NSUB, int GPT, bool PLANE, int NB, int B0, int B1, int C>
+__device__ __forceinline__ void group_step(const BlockDesc *dsc, int strip, int g, int n_kt, bool more, int cn,
+                                           const uint16_t *const *rowp, uint16_t *xs, uint16_t *lut_lds,
+                                           Stager<NSUB, PLANE, B0, B1, NB> &stg, f32x4 (*acc)[NSUB]) {
+  Group<B0, PLANE> g0;
+  Group<B1, PLANE> g1;
+  load_group<B0, PLANE, C, GPT>(dsc[0], strip, g, n_kt, g0);
+  if constexpr (NB == 2) load_group<B1, PLANE, C, GPT>(dsc[1], strip, g, n_kt, g1);
+  if (more) stg.load(dsc, rowp, strip, g + 1, n_kt, cn);
+  if constexpr (PLANE) compute_plane<NSUB, NB, B0, B1, C>(g0, g1, xs, lut_lds, acc);
+  else compute_int<NSUB, NB, B0, B1, C, GPT>(g0, g1, xs, acc);
+  if (more) {
+    __syncthreads();
+    stg.store(xs, lut_lds, cn);
+    __syncthreads();
+  }
+}
+
+// The streaming loop over tile groups [g_begin, g_end) of the NB blocks.
+template <int NSUB, int GPT, bool PLANE, int NB, int B0, int B1>
+__device__ __forceinline__ void stream_blocks(const BlockDesc *dsc, int strip, int g_begin, int g_end,
+                                              const uint16_t *const *rowp, uint16_t *xs, uint16_t *lut_lds,
+                                              f32x4 (*acc)[NSUB]) {
+  const int n_kt = dsc[0].K / kTileK;
+  const int full = n_kt / 4;                  // groups with 4 tiles
+  Stager<NSUB, PLANE, B0, B1, NB> stg;
+  {
+    const int c = std::min(4, n_kt - 4 * g_begin);
+    stg.load(dsc, rowp, strip, g_begin, n_kt, c);
+    stg.store(xs, lut_lds, c);
+    __syncthreads();
+  }
+  const int g_full_end = std::min(g_end, full);
+#pragma unroll 1
+  for (int g = g_begin; g < g_full_end; ++g) {
+    const bool more = g + 1 < g_end;
+    const int cn = more ? std::min(4, n_kt - 4 * (g + 1)) : 0;
+    group_step<NSUB, GPT, PLANE, NB, B0, B1, 4>(dsc, strip, g, n_kt, more, cn, rowp, xs, lut_lds, stg, acc);
+  }
+  if (g_end > full) {                         // the ragged last group
+    switch (n_kt - 4 * full) {
+      case 1: group_step<NSUB, GPT, PLANE, NB, B0, B1, 1>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
+      case 2: group_step<NSUB, GPT, PLANE, NB, B0, B1, 2>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
+      default: group_step<NSUB, GPT, PLANE, NB, B0, B1, 3>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
+    }
+  }
+}
+
+// Wave-uniform row pointers of the staged activations: pass p loads chunk
+// row 4p + wave (clamped to the last valid row).
+template <int NSUB>
+__device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a, const Chunk &ch, bool gather) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < NSUB * 4; ++p) {
+    const int m = std::min(4 * p + wave, ch.cnt - 1);
+    const uint16_t *ptr;
+    if (gather) ptr = a.x + (int64_t)(a.sorted_pairs[ch.base + m] / a.k) * a.H;
+    else ptr = a.h + (int64_t)(ch.base + m) * a.I;
+    const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    rowp[p] = reinterpret_cast<const uint16_t *>(((uint64_t)hi << 32) | lo);
+  }
+}
+
+template <int NSUB, int GPT, bool PLANE, int BG, int BU>
+__device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *xs,
+                                            uint16_t *lut_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t *rowp[NSUB * 4];
+  row_ptrs<NSUB>(rowp, a, ch, true);
+  const BlockDesc *dsc = a.desc + 3 * ch.e;
+  f32x4 acc[2][NSUB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_g4 = (a.H / kTileK + 3) / 4;
+  stream_blocks<NSUB, GPT, PLANE, 2, BG, BU>(dsc, strip, 0, n_g4, rowp, xs, lut_lds, acc);
+  const int row = strip * 16 + (lane & 15);
+  if (a.comp_on) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint16_t *zb = a.z_gu + b * a.RZ;
+      if (a.r > 0) lowrank_epi<NSUB>(dsc[b].U, a.r, a.Rp, row, zb, 2 * a.RZ, ch, acc[b]);
+      if (a.rs > 0) lowrank_epi<NSUB>(dsc[b].Us, a.rs, a.Rsp, row, zb + a.Rp, 2 * a.RZ, ch, acc[b]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * s + 4 * (lane >> 4) + i;
+      if (m < ch.cnt) {
+        const float g = acc[0][s][i], u = acc[1][s][i];
+        const float hv = g / (1.0f + __expf(-g)) * u;
+        a.h[(int64_t)(ch.base + m) * a.I + row] = __builtin_bit_cast(uint16_t, (f16)hv);
+      }
+    }
+  }
+}
+
+template <int NSUB, int GPT, bool PLANE, int BD>
+__device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int strip, int split,
+                                          uint16_t *xs, uint16_t *lut_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t *rowp[NSUB * 4];
+  row_ptrs<NSUB>(rowp, a, ch, false);
+  const BlockDesc *dsc = a.desc + 3 * ch.e + 2;
+  f32x4 acc[1][NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_g4 = (a.I / kTileK + 3) / 4;
+  const int g0 = (int)((int64_t)n_g4 * split / a.splits);
+  const int g1 = (int)((int64_t)n_g4 * (split + 1) / a.splits);
+  if (g1 > g0) stream_blocks<NSUB, GPT, PLANE, 1, BD, BD>(dsc, strip, g0, g1, rowp, xs, lut_lds, acc);
+  const int row = strip * 16 + (lane & 15);
+  if (a.comp_on && split == 0) {
+    if (a.r > 0) lowrank_epi<NSUB>(dsc[0].U, a.r, a.Rp, row, a.z_d, a.RZ, ch, acc[0]);
+    if (a.rs > 0) lowrank_epi<NSUB>(dsc[0].Us, a.rs, a.Rsp, row, a.z_d + a.Rp, a.RZ, ch, acc[0]);
+  }
+  float *yp = a.ypart + (int64_t)split * a.P * a.H;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * s + 4 * (lane >> 4) + i;
+      if (m < ch.cnt) yp[(int64_t)(ch.base + m) * a.H + row] = acc[0][s][i];
+    }
+  }
+}
+
+__device__ __forceinline__ uint16_t *dyn_lds() {
+  extern __shared__ __attribute__((aligned(16))) uint16_t moeq_dyn_lds[];
+  return moeq_dyn_lds;
+}
+
+// Chunk classes: NSUB = 1, 2, 4 token tiles (<= 16, <= 32, <= 64 tokens).
+// One launch per class present; a workgroup whose chunk is of another class
+// exits at once.
+__device__ __forceinline__ int nsub_of(int cnt) { return cnt <= 16 ? 1 : (cnt <= 32 ? 2 : 4); }
+
+// gate/up: grid.x = max_chunks * (I / 64)
+template <int NSUB, int GPT, bool PLANE>
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 2) gateup_kernel(FfnArgs a) {
+  uint16_t *xs = dyn_lds();
+  const int wave = threadIdx.x >> 6;
+  const int n_sg = a.I / (16 * kStripsPerWG);
+  const int chunk = blockIdx.x / n_sg, sg = blockIdx.x % n_sg;
+  Chunk ch;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
+  const int strip = sg * kStripsPerWG + wave;
+  uint16_t *ll = xs + NSUB * 16 * kXStride + (PLANE ? wave * 2 * kLutBlk : 0);
+  const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
+  switch (bg * 4 + bu) {
+    case 2 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 2, 2>(a, ch, strip, xs, ll); break;
+    case 2 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 2, 3>(a, ch, strip, xs, ll); break;
+    case 2 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 2, 4>(a, ch, strip, xs, ll); break;
+    case 3 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 3, 2>(a, ch, strip, xs, ll); break;
+    case 3 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 3, 3>(a, ch, strip, xs, ll); break;
+    case 3 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 3, 4>(a, ch, strip, xs, ll); break;
+    case 4 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 4, 2>(a, ch, strip, xs, ll); break;
+    case 4 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 4, 3>(a, ch, strip, xs, ll); break;
+    default: gateup_body<NSUB, GPT, PLANE, 4, 4>(a, ch, strip, xs, ll); break;
+  }
+}
+
+// down: grid.x = max_chunks * (H / 64) * splits
+template <int NSUB, int GPT, bool PLANE>
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 2) down_kernel(FfnArgs a) {
+  uint16_t *xs = dyn_lds();
+  const int wave = threadIdx.x >> 6;
+  const int n_sg = a.H / (16 * kStripsPerWG);
+  const int split = blockIdx.x % a.splits;
+  const int rest = blockIdx.x / a.splits;
+  const int chunk = rest / n_sg, sg = rest % n_sg;
+  Chunk ch;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
+  const int strip = sg * kStripsPerWG + wave;
+  uint16_t *ll = xs + NSUB * 16 * kXStride + (PLANE ? wave * kLutBlk : 0);
+  switch (a.desc[3 * ch.e + 2].bits) {
+    case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, strip, split, xs, ll); break;
+    case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, strip, split, xs, ll); break;
+    default: down_body<NSUB, GPT, PLANE, 4>(a, ch, strip, split, xs, ll); break;
+  }
+}
+
+inline size_t stream_lds_bytes(bool plane, int nsub, int nb) {
+  size_t b = (size_t)nsub * 16 * kXStride * 2;
+  if (plane) b += (size_t)4 * nb * kLutBlk * 2;
+  return b;
+}
+
+// Launch helpers for one (GPT, PLANE) class, instantiated in the .hip files.
+template <int GPT, bool PLANE>
+void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, 2), s, a);
+  if (a.nsub_max >= 2)
+    hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, 2), s, a);
+  if (a.nsub_max >= 3)
+    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, 2), s, a);
+}
+
+template <int GPT, bool PLANE>
+void launch_down_class(const FfnArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, 1), s, a);
+  if (a.nsub_max >= 2)
+    hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, 1), s, a);
+  if (a.nsub_max >= 3)
+    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, 1), s, a);
+}
+
+void launch_gateup_g128(const FfnArgs &a, int grid, hipStream_t s);
+void launch_gateup_g64(const FfnArgs &a, int grid, hipStream_t s);
+void launch_gateup_plane(const FfnArgs &a, int grid, hipStream_t s);
+void launch_down_g128(const FfnArgs &a, int grid, hipStream_t s);
+void launch_down_g64(const FfnArgs &a, int grid, hipStream_t s);
+void launch_down_plane(const FfnArgs &a, int grid, hipStream_t s);
+
+}  // namespace moeq

@@ -1,0 +1,11 @@
+// Instantiation of the weight-streaming down kernels for one layer class
+// (see stream.hpp).
+#include "stream.hpp"
+
+namespace moeq {
+
+void launch_down_plane(const FfnArgs &a, int grid, hipStream_t s) {
+  launch_down_class<1, true>(a, grid, s);
+}
+
+}  // namespace moeq
