@@ -12,7 +12,8 @@ namespace moeq {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
-  size_t z_gu, z_d, h, ypart, total;
+  size_t zp_gu, zp_d, h, ypart, total;
+  int ks_gu, ks_d;
 };
 
 static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
@@ -20,8 +21,15 @@ static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options
   const int P = T * k;
   const int n_g4 = (L->dims.I / kTileK + 3) / 4;
   // few tokens: split the long down-projection K for more waves in flight
-  int s = P <= 256 ? 4 : 1;
+  int s = P <= 256 ? 8 : 1;
   return std::max(1, std::min(s, n_g4));
+}
+
+// K splits of a low-rank projection over K columns: few tokens leave few
+// workgroups, so cut K into ~1024-column pieces; many tokens need none.
+static int pick_ks(int P, int K) {
+  if (P > 256) return 1;
+  return std::max(1, std::min(16, K / 1024));
 }
 
 static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
@@ -29,9 +37,11 @@ static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
   const int Rp = (L->dims.r + 31) / 32 * 32, Rsp = (L->dims.rs + 31) / 32 * 32;
   const int RZ = Rp + Rsp;
   Ws w;
+  w.ks_gu = pick_ks((int)P, L->dims.H);
+  w.ks_d = pick_ks((int)P, L->dims.I);
   size_t off = 0;
-  w.z_gu = off; off = al256(off + (size_t)P * 2 * RZ * 2);
-  w.z_d = off; off = al256(off + (size_t)P * RZ * 2);
+  w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * P * 2 * RZ * 4);
+  w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
   w.h = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.ypart = off; off = al256(off + (size_t)splits * P * L->dims.H * 4);
   w.total = off;
@@ -84,8 +94,12 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.r = D.r; a.rs = D.rs;
   a.Rp = (D.r + 31) / 32 * 32; a.Rsp = (D.rs + 31) / 32 * 32; a.RZ = a.Rp + a.Rsp;
   a.comp_on = (n_comp > 0 && a.RZ > 0) ? 1 : 0;
-  a.z_gu = reinterpret_cast<uint16_t *>(wb + w.z_gu);
-  a.z_d = reinterpret_cast<uint16_t *>(wb + w.z_d);
+  a.zp_gu = reinterpret_cast<float *>(wb + w.zp_gu);
+  a.zp_d = reinterpret_cast<float *>(wb + w.zp_d);
+  a.ks_gu = w.ks_gu;
+  a.ks_d = w.ks_d;
+  a.ks_stride_gu = (int64_t)T * k * 2 * a.RZ;
+  a.ks_stride_d = (int64_t)T * k * a.RZ;
   a.h = reinterpret_cast<uint16_t *>(wb + w.h);
   a.ypart = reinterpret_cast<float *>(wb + w.ypart);
   a.splits = splits;
@@ -109,7 +123,7 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
     prof_end("lowrank_project_down", stream);
   }
   prof_begin("down_stream", stream);
-  launch_down_stream(a, mc * (D.H / 64) * splits, stream);
+  launch_down_stream(a, mc * (D.H / 128) * splits, stream);
   prof_end("down_stream", stream);
   prof_begin("combine", stream);
   launch_combine(a, y, y_dtype == MOEQ_F32, stream);

@@ -20,8 +20,10 @@ struct FfnArgs {
   int r, rs, Rp, Rsp, RZ;
   int comp_on;
   int G, fmt;
-  uint16_t *z_gu;   // [P][2][RZ] fp16
-  uint16_t *z_d;    // [P][RZ] fp16
+  float *zp_gu;     // [ks_gu][P][2][RZ] fp32 partial V x (summed by the consumer)
+  float *zp_d;      // [ks_d][P][RZ] fp32 partial V_down h
+  int ks_gu, ks_d;  // K splits of the two projections
+  int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
   uint16_t *h;      // [P][I] fp16
   float *ypart;     // [splits][P][H] fp32
   int splits;
@@ -52,10 +54,12 @@ __device__ __forceinline__ bool find_chunk(const int32_t *__restrict__ off, int 
     const int excl = carry + incl - nc;
     const uint64_t hit = __ballot(c >= excl && c < excl + nc);
     if (hit) {
+      // every lane holds the same values; readfirstlane makes that visible
+      // to the compiler so they live in scalar registers
       const int src = __builtin_ctzll(hit);
-      const int ex = __shfl(excl, src, kWave);
-      const int cn = __shfl(cnt, src, kWave);
-      out->e = b + src;
+      const int ex = __builtin_amdgcn_readfirstlane(__shfl(excl, src, kWave));
+      const int cn = __builtin_amdgcn_readfirstlane(__shfl(cnt, src, kWave));
+      out->e = __builtin_amdgcn_readfirstlane(b + src);
       out->m0 = (c - ex) * kMT;
       out->cnt = std::min(kMT, cn - out->m0);
       out->base = off[out->e] + out->m0;

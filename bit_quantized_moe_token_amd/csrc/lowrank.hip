@@ -10,11 +10,13 @@
 
 namespace moeq {
 
-// z[pos][slot] = V v for compensated pairs (zero otherwise).  One 16-token
-// tile per workgroup, 4 waves split K and reduce through LDS in fixed order.
-// grid.x = max_chunks * 4 tiles, grid.y = (#blocks) * (Rp + Rsp) / 16.
-// mode 0: v = x[token] (gate/up, blk0 = 0, nblk = 2); mode 1: v = h[pos]
-// (down, blk0 = 2, nblk = 1).
+// Partial z[pos][slot] = V v over one K range for compensated pairs (zero
+// for the others); the consumer kernels sum the ks partials in fixed order.
+// One 16-token tile per workgroup, 4 waves split the range and reduce
+// through LDS in fixed order.
+// grid.x = max_chunks * 4 tiles, grid.y = (#blocks) * (Rp + Rsp) / 16,
+// grid.z = ks.  mode 0: v = x[token] (gate/up blocks); mode 1: v = h[pos]
+// (down block).
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode) {
   __shared__ f32x4 s_part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -27,10 +29,11 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const int set = rem < a.Rp / 16 ? 0 : 1;
   const int it = set ? rem - a.Rp / 16 : rem;
   const int blk = mode == 0 ? bi : 2;
-  const BlockDesc d = a.desc[3 * ch.e + blk];
+  const BlockDesc &d = a.desc[3 * ch.e + blk];
   const uint16_t *V = set ? d.Vs : d.V;
   const int R = set ? a.rs : a.r;
   const int K = d.K;
+  const int KS = mode == 0 ? a.ks_gu : a.ks_d;
   const int i = 16 * it + (lane & 15);
   const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
   const int pos = ch.base + mloc;
@@ -40,7 +43,8 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const uint16_t *vrow = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
   const bool vi = i < R;
   const int nsteps = K / 32;
-  const int s0 = nsteps * wave / 4, s1 = nsteps * (wave + 1) / 4;
+  const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
+  const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int st = s0; st < s1; ++st) {
     f16x8 b = vi ? load_a(vrow + 32 * st) : pack_b(0, 0, 0, 0);
@@ -56,7 +60,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
 #pragma unroll
     for (int q = 0; q < 4; ++q) sum[q] += p[q];
   }
-  uint16_t *zbase = mode == 0 ? a.z_gu : a.z_d;
+  float *zbase = mode == 0 ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
   const int zstride = mode == 0 ? 2 * a.RZ : a.RZ;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -64,9 +68,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     if (m < ch.cnt) {
       const int p2 = ch.base + m;
       const bool comp = (a.sorted_pairs[p2] % a.k) < a.n_comp;
-      const f16 v = comp ? (f16)sum[q] : (f16)0.0f;
-      zbase[(int64_t)p2 * zstride + bi * a.RZ + set * a.Rp + 16 * it + (lane & 15)] =
-          __builtin_bit_cast(uint16_t, v);
+      zbase[(int64_t)p2 * zstride + bi * a.RZ + set * a.Rp + 16 * it + (lane & 15)] = comp ? sum[q] : 0.0f;
     }
   }
 }
@@ -104,6 +106,7 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 }
 
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
+  grid.z = mode == 0 ? a.ks_gu : a.ks_d;
   hipLaunchKernelGGL(lowrank_project_kernel, grid, dim3(256), 0, s, a, mode);
 }
 

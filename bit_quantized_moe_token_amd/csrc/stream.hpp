@@ -214,30 +214,32 @@ __device__ __forceinline__ void compute_plane(const Group<Q0, true> &g0, const G
   }
 }
 
-// ---- activation staging: NSUB*16 rows x 512 columns of group g4.  Pass p
-// of NSUB*4 loads row 4p + wave (wave-uniform row pointer), lane = 16 B.
-template <int NSUB>
+// ---- activation staging: NSUB*16 rows x 512 columns of group g4, by all
+// NW waves of the workgroup.  Pass p loads row NW*p + wave (wave-uniform
+// row pointer); a lane moves 16 B.
+template <int NSUB, int NW>
 struct XStage {
-  u32x4 v[NSUB * 4];
+  static constexpr int NP = NSUB * 16 / NW;
+  u32x4 v[NP];
 };
 
-template <int NSUB>
-__device__ __forceinline__ void stage_load(XStage<NSUB> &st, const uint16_t *const *rowp, int g4, int c) {
+// Lanes past the group's c tiles (ragged last group) re-read the group's
+// first columns instead of branching; their LDS columns are never read.
+template <int NSUB, int NW>
+__device__ __forceinline__ void stage_load(XStage<NSUB, NW> &st, const uint16_t *const *rowp, int g4, int c) {
   const int lane = threadIdx.x & 63;
-  const int col = 4 * kTileK * g4 + 8 * lane;      // halves
+  const int col = 4 * kTileK * g4 + 8 * (lane < 16 * c ? lane : 0);      // halves
 #pragma unroll
-  for (int p = 0; p < NSUB * 4; ++p) {
-    if (lane < 16 * c) st.v[p] = gld<u32x4>(rowp[p] + col);
-  }
+  for (int p = 0; p < XStage<NSUB, NW>::NP; ++p) st.v[p] = gld<u32x4>(rowp[p] + col);
 }
 
-template <int NSUB>
-__device__ __forceinline__ void stage_store(const XStage<NSUB> &st, uint16_t *xs, int c) {
+template <int NSUB, int NW>
+__device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t *xs, int c) {
+  (void)c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int p = 0; p < NSUB * 4; ++p) {
-    if (lane < 16 * c) *reinterpret_cast<u32x4 *>(xs + (4 * p + wave) * kXStride + 8 * lane) = st.v[p];
-  }
+  for (int p = 0; p < XStage<NSUB, NW>::NP; ++p)
+    *reinterpret_cast<u32x4 *>(xs + (NW * p + wave) * kXStride + 8 * lane) = st.v[p];
 }
 
 // LUT staging of one wave's strip for a group: 4 tiles x 16 rows x NQ
@@ -251,123 +253,161 @@ template <int Q>
 __device__ __forceinline__ void lut_load(const BlockDesc &d, int strip, int g4, int n_kt, int c, LutStage<Q> &ls) {
   constexpr int NQ = 1 << Q;
   const int lane = threadIdx.x & 63;
-  const uint16_t *p = d.lut + lut_index(strip, 4 * g4, 0, 0, n_kt, NQ) + lane * NQ;
-  if (lane < 16 * c) {
+  const uint16_t *p = d.lut + lut_index(strip, 4 * g4, 0, 0, n_kt, NQ) + (lane < 16 * c ? lane : 0) * NQ;
 #pragma unroll
-    for (int i = 0; i < NQ / 2; ++i) ls.v[i] = gld<uint32_t>(p + 2 * i);
-  }
+  for (int i = 0; i < NQ / 2; ++i) ls.v[i] = gld<uint32_t>(p + 2 * i);
 }
 
 template <int Q>
 __device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, int c) {
+  (void)c;
   constexpr int NQ = 1 << Q;
   const int lane = threadIdx.x & 63;
-  if (lane < 16 * c) {
 #pragma unroll
-    for (int i = 0; i < NQ / 2; ++i) reinterpret_cast<uint32_t *>(dst + lane * NQ)[i] = ls.v[i];
+  for (int i = 0; i < NQ / 2; ++i) reinterpret_cast<uint32_t *>(dst + lane * NQ)[i] = ls.v[i];
+}
+
+// z of the chunk's pairs in LDS: sums the ks fp32 partials of the
+// projection kernel (all loads issued before any add) and rounds to fp16.
+// zs layout: [NSUB*16 rows][width] fp16 with width = nset * RZ (RZ padded
+// columns per block); src column base = col0 within each partial row.
+template <int NSUB, int NW>
+__device__ __forceinline__ void z_prologue(const float *zpart, int zstride, int64_t kstride, int KS,
+                                           int width, const Chunk &ch, uint16_t *zs) {
+  const int tid = threadIdx.x;
+  const int n4 = NSUB * 16 * width / 4;                  // float4 outputs
+  for (int o = tid; o < n4; o += NW * 64) {
+    const int row = (4 * o) / width, col = (4 * o) % width;
+    const int m = std::min(row, ch.cnt - 1);
+    const float *src = zpart + (int64_t)(ch.base + m) * zstride + col;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    for (; k + 4 <= KS; k += 4) {
+      const f32x4 v0 = gld<f32x4>(src + (k + 0) * kstride), v1 = gld<f32x4>(src + (k + 1) * kstride);
+      const f32x4 v2 = gld<f32x4>(src + (k + 2) * kstride), v3 = gld<f32x4>(src + (k + 3) * kstride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v0[i] + v1[i] + v2[i] + v3[i];
+    }
+    for (; k < KS; ++k) {
+      const f32x4 v = gld<f32x4>(src + k * kstride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v[i];
+    }
+    u32x2 h;
+    h[0] = as_u32(f16x2{(f16)sum[0], (f16)sum[1]});
+    h[1] = as_u32(f16x2{(f16)sum[2], (f16)sum[3]});
+    *reinterpret_cast<u32x2 *>(zs + row * width + col) = h;
   }
 }
 
-// Low-rank epilogue: acc += U z for one factor set (z fp16 rows of the
-// chunk's pairs; zero rows for uncompensated pairs and columns >= R).
+// Low-rank epilogue: acc += U z for one factor set (z rows in LDS, zero for
+// uncompensated pairs and for columns >= R).
 template <int NSUB>
-__device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, int row,
-                                            const uint16_t *zbase, int zstride, const Chunk &ch,
-                                            f32x4 *acc) {
+__device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, int row, const uint16_t *zs,
+                                            int zwidth, f32x4 *acc) {
   const int lane = threadIdx.x & 63, kq = lane >> 4;
   for (int ks = 0; ks < Rpad / 32; ++ks) {
     const int col = 32 * ks + 8 * kq;
     f16x8 bop = pack_b(0, 0, 0, 0);
     if (col < R) bop = load_a(U + (int64_t)row * R + col);
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int m = std::min(16 * s + (lane & 15), ch.cnt - 1);
-      acc[s] = mfma16(load_a(zbase + (int64_t)(ch.base + m) * zstride + col), bop, acc[s]);
-    }
+    for (int s = 0; s < NSUB; ++s)
+      acc[s] = mfma16(*reinterpret_cast<const f16x8 *>(zs + (16 * s + (lane & 15)) * zwidth + col), bop, acc[s]);
   }
 }
 
-// Stage group g's activations (and bit-plane LUTs) into LDS: load, then
-// (after the caller's barrier) store.
-template <int NSUB, bool PLANE, int B0, int B1, int NB>
+// Stage group g's activations (and the two streams' bit-plane LUTs) into
+// LDS: load, then (after the caller's barrier) store.
+template <int NSUB, int NW, bool PLANE, int B0, int B1>
 struct Stager {
-  XStage<NSUB> st;
+  XStage<NSUB, NW> st;
   LutStage<B0> l0;
   LutStage<B1> l1;
-  __device__ __forceinline__ void load(const BlockDesc *dsc, const uint16_t *const *rowp, int strip, int g4,
-                                       int n_kt, int c) {
-    stage_load<NSUB>(st, rowp, g4, c);
+  __device__ __forceinline__ void load(const BlockDesc &d0, const BlockDesc &d1, const uint16_t *const *rowp,
+                                       int s0, int s1, int g4, int n_kt, int c) {
+    stage_load<NSUB, NW>(st, rowp, g4, c);
     if constexpr (PLANE) {
-      lut_load<B0>(dsc[0], strip, g4, n_kt, c, l0);
-      if constexpr (NB == 2) lut_load<B1>(dsc[1], strip, g4, n_kt, c, l1);
+      lut_load<B0>(d0, s0, g4, n_kt, c, l0);
+      lut_load<B1>(d1, s1, g4, n_kt, c, l1);
     }
   }
   __device__ __forceinline__ void store(uint16_t *xs, uint16_t *lut_lds, int c) {
-    stage_store<NSUB>(st, xs, c);
+    stage_store<NSUB, NW>(st, xs, c);
     if constexpr (PLANE) {
       lut_store<B0>(l0, lut_lds, c);
-      if constexpr (NB == 2) lut_store<B1>(l1, lut_lds + kLutBlk, c);
+      lut_store<B1>(l1, lut_lds + kLutBlk, c);
     }
   }
 };
 
-// One group of C tiles for the NB blocks (bitwidths B0, B1).
-template <int NSUB, int GPT, bool PLANE, int NB, int B0, int B1, int C>
-__device__ __forceinline__ void group_step(const BlockDesc *dsc, int strip, int g, int n_kt, bool more, int cn,
-                                           const uint16_t *const *rowp, uint16_t *xs, uint16_t *lut_lds,
-                                           Stager<NSUB, PLANE, B0, B1, NB> &stg, f32x4 (*acc)[NSUB]) {
-  Group<B0, PLANE> g0;
-  Group<B1, PLANE> g1;
-  load_group<B0, PLANE, C, GPT>(dsc[0], strip, g, n_kt, g0);
-  if constexpr (NB == 2) load_group<B1, PLANE, C, GPT>(dsc[1], strip, g, n_kt, g1);
-  if (more) stg.load(dsc, rowp, strip, g + 1, n_kt, cn);
-  if constexpr (PLANE) compute_plane<NSUB, NB, B0, B1, C>(g0, g1, xs, lut_lds, acc);
-  else compute_int<NSUB, NB, B0, B1, C, GPT>(g0, g1, xs, acc);
-  if (more) {
-    __syncthreads();
-    stg.store(xs, lut_lds, cn);
-    __syncthreads();
-  }
+template <int NSUB, int B0, int B1, bool PLANE, int C, int GPT>
+__device__ __forceinline__ void compute_two(const Group<B0, PLANE> &g0, const Group<B1, PLANE> &g1,
+                                            const uint16_t *xs, const uint16_t *lut, f32x4 (*acc)[NSUB]) {
+  if constexpr (PLANE) compute_plane<NSUB, 2, B0, B1, C>(g0, g1, xs, lut, acc);
+  else compute_int<NSUB, 2, B0, B1, C, GPT>(g0, g1, xs, acc);
 }
 
-// The streaming loop over tile groups [g_begin, g_end) of the NB blocks.
-template <int NSUB, int GPT, bool PLANE, int NB, int B0, int B1>
-__device__ __forceinline__ void stream_blocks(const BlockDesc *dsc, int strip, int g_begin, int g_end,
-                                              const uint16_t *const *rowp, uint16_t *xs, uint16_t *lut_lds,
-                                              f32x4 (*acc)[NSUB]) {
-  const int n_kt = dsc[0].K / kTileK;
-  const int full = n_kt / 4;                  // groups with 4 tiles
-  Stager<NSUB, PLANE, B0, B1, NB> stg;
+// Streams tile groups [g_begin, g_end) of two weight streams per wave —
+// (block d0, strip s0) and (block d1, strip s1) — that share one activation
+// fragment per MFMA.  The NW waves of the workgroup share the staged
+// activations.  Per group: this group's code loads first, then the next
+// group's activations (publishing those never waits for the codes), then
+// decode + MFMA; the other resident workgroups cover the load latency.
+template <int NSUB, int NW, int GPT, bool PLANE, int B0, int B1>
+__device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc &d1, int s0, int s1,
+                                           int g_begin, int g_end, const uint16_t *const *rowp, uint16_t *xs,
+                                           uint16_t *lut_lds, f32x4 (*acc)[NSUB]) {
+  const int n_kt = d0.K / kTileK;
+  const int full = n_kt / 4;                   // groups with 4 tiles
+  const int g_full_end = std::min(g_end, full);
+  Stager<NSUB, NW, PLANE, B0, B1> stg;
   {
     const int c = std::min(4, n_kt - 4 * g_begin);
-    stg.load(dsc, rowp, strip, g_begin, n_kt, c);
+    stg.load(d0, d1, rowp, s0, s1, g_begin, n_kt, c);
     stg.store(xs, lut_lds, c);
     __syncthreads();
   }
-  const int g_full_end = std::min(g_end, full);
 #pragma unroll 1
   for (int g = g_begin; g < g_full_end; ++g) {
     const bool more = g + 1 < g_end;
     const int cn = more ? std::min(4, n_kt - 4 * (g + 1)) : 0;
-    group_step<NSUB, GPT, PLANE, NB, B0, B1, 4>(dsc, strip, g, n_kt, more, cn, rowp, xs, lut_lds, stg, acc);
+    Group<B0, PLANE> c0;
+    Group<B1, PLANE> c1;
+    load_group<B0, PLANE, 4, GPT>(d0, s0, g, n_kt, c0);
+    load_group<B1, PLANE, 4, GPT>(d1, s1, g, n_kt, c1);
+    if (more) stg.load(d0, d1, rowp, s0, s1, g + 1, n_kt, cn);
+    compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xs, lut_lds, acc);
+    if (more) {
+      __syncthreads();
+      stg.store(xs, lut_lds, cn);
+      __syncthreads();
+    }
   }
-  if (g_end > full) {                         // the ragged last group
+  if (g_end > full) {                          // the ragged last group
+    Group<B0, PLANE> t0;
+    Group<B1, PLANE> t1;
     switch (n_kt - 4 * full) {
-      case 1: group_step<NSUB, GPT, PLANE, NB, B0, B1, 1>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
-      case 2: group_step<NSUB, GPT, PLANE, NB, B0, B1, 2>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
-      default: group_step<NSUB, GPT, PLANE, NB, B0, B1, 3>(dsc, strip, full, n_kt, false, 0, rowp, xs, lut_lds, stg, acc); break;
+      case 1:
+        load_group<B0, PLANE, 1, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 1, GPT>(d1, s1, full, n_kt, t1);
+        compute_two<NSUB, B0, B1, PLANE, 1, GPT>(t0, t1, xs, lut_lds, acc); break;
+      case 2:
+        load_group<B0, PLANE, 2, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 2, GPT>(d1, s1, full, n_kt, t1);
+        compute_two<NSUB, B0, B1, PLANE, 2, GPT>(t0, t1, xs, lut_lds, acc); break;
+      default:
+        load_group<B0, PLANE, 3, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 3, GPT>(d1, s1, full, n_kt, t1);
+        compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xs, lut_lds, acc); break;
     }
   }
 }
 
 // Wave-uniform row pointers of the staged activations: pass p loads chunk
-// row 4p + wave (clamped to the last valid row).
-template <int NSUB>
+// row NW*p + wave (clamped to the last valid row).
+template <int NSUB, int NW>
 __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a, const Chunk &ch, bool gather) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int p = 0; p < NSUB * 4; ++p) {
-    const int m = std::min(4 * p + wave, ch.cnt - 1);
+  for (int p = 0; p < XStage<NSUB, NW>::NP; ++p) {
+    const int m = std::min(NW * p + wave, ch.cnt - 1);
     const uint16_t *ptr;
     if (gather) ptr = a.x + (int64_t)(a.sorted_pairs[ch.base + m] / a.k) * a.H;
     else ptr = a.h + (int64_t)(ch.base + m) * a.I;
@@ -378,27 +418,40 @@ __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a
   }
 }
 
+// LDS layout of both stream kernels: [x staging | z rows | LUTs].
+template <int NSUB>
+__device__ __forceinline__ int zs_offset() { return NSUB * 16 * kXStride; }
+
+// gate/up: 4 waves, each streams the gate and the up rows of one 16-row
+// strip; h = SiLU(gate) * up is formed in registers.
 template <int NSUB, int GPT, bool PLANE, int BG, int BU>
-__device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *xs,
+__device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *lds,
                                             uint16_t *lut_lds) {
   const int lane = threadIdx.x & 63;
-  const uint16_t *rowp[NSUB * 4];
-  row_ptrs<NSUB>(rowp, a, ch, true);
-  const BlockDesc *dsc = a.desc + 3 * ch.e;
+  uint16_t *xs = lds;
+  uint16_t *zs = lds + zs_offset<NSUB>();
+  const int zw = 2 * a.RZ;
+  if (a.comp_on) {
+    z_prologue<NSUB, 4>(a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    __syncthreads();
+  }
+  const uint16_t *rowp[XStage<NSUB, 4>::NP];
+  row_ptrs<NSUB, 4>(rowp, a, ch, true);
+  const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];   // scalar loads
   f32x4 acc[2][NSUB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.H / kTileK + 3) / 4;
-  stream_blocks<NSUB, GPT, PLANE, 2, BG, BU>(dsc, strip, 0, n_g4, rowp, xs, lut_lds, acc);
+  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, lut_lds, acc);
   const int row = strip * 16 + (lane & 15);
   if (a.comp_on) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const uint16_t *zb = a.z_gu + b * a.RZ;
-      if (a.r > 0) lowrank_epi<NSUB>(dsc[b].U, a.r, a.Rp, row, zb, 2 * a.RZ, ch, acc[b]);
-      if (a.rs > 0) lowrank_epi<NSUB>(dsc[b].Us, a.rs, a.Rsp, row, zb + a.Rp, 2 * a.RZ, ch, acc[b]);
+      const BlockDesc &d = b ? du : dg;
+      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b]);
+      if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[b]);
     }
   }
 #pragma unroll
@@ -415,32 +468,49 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   }
 }
 
+// down: 4 waves, each streams two 16-row strips of the down block over the
+// split's K range.
 template <int NSUB, int GPT, bool PLANE, int BD>
-__device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int strip, int split,
-                                          uint16_t *xs, uint16_t *lut_lds) {
+__device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int sg, int split, uint16_t *lds,
+                                          uint16_t *lut_lds) {
   const int lane = threadIdx.x & 63;
-  const uint16_t *rowp[NSUB * 4];
-  row_ptrs<NSUB>(rowp, a, ch, false);
-  const BlockDesc *dsc = a.desc + 3 * ch.e + 2;
-  f32x4 acc[1][NSUB];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint16_t *xs = lds;
+  uint16_t *zs = lds + zs_offset<NSUB>();
+  const int zw = a.RZ;
+  const bool epi = a.comp_on && split == 0;
+  if (epi) {
+    z_prologue<NSUB, 4>(a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, zw, ch, zs);
+    __syncthreads();
+  }
+  const uint16_t *rowp[XStage<NSUB, 4>::NP];
+  row_ptrs<NSUB, 4>(rowp, a, ch, false);
+  const BlockDesc d = a.desc[3 * ch.e + 2];                          // scalar loads
+  f32x4 acc[2][NSUB];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.I / kTileK + 3) / 4;
   const int g0 = (int)((int64_t)n_g4 * split / a.splits);
   const int g1 = (int)((int64_t)n_g4 * (split + 1) / a.splits);
-  if (g1 > g0) stream_blocks<NSUB, GPT, PLANE, 1, BD, BD>(dsc, strip, g0, g1, rowp, xs, lut_lds, acc);
-  const int row = strip * 16 + (lane & 15);
-  if (a.comp_on && split == 0) {
-    if (a.r > 0) lowrank_epi<NSUB>(dsc[0].U, a.r, a.Rp, row, a.z_d, a.RZ, ch, acc[0]);
-    if (a.rs > 0) lowrank_epi<NSUB>(dsc[0].Us, a.rs, a.Rsp, row, a.z_d + a.Rp, a.RZ, ch, acc[0]);
-  }
+  const int st0 = 8 * sg + 2 * wave, st1 = st0 + 1;
+  if (g1 > g0) stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, lut_lds, acc);
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
+  for (int b = 0; b < 2; ++b) {
+    const int row = (b ? st1 : st0) * 16 + (lane & 15);
+    if (epi) {
+      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b]);
+      if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + a.Rp, zw, acc[b]);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * s + 4 * (lane >> 4) + i;
-      if (m < ch.cnt) yp[(int64_t)(ch.base + m) * a.H + row] = acc[0][s][i];
+    for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * s + 4 * (lane >> 4) + i;
+        if (m < ch.cnt) yp[(int64_t)(ch.base + m) * a.H + row] = acc[b][s][i];
+      }
     }
   }
 }
@@ -455,74 +525,80 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
 // exits at once.
 __device__ __forceinline__ int nsub_of(int cnt) { return cnt <= 16 ? 1 : (cnt <= 32 ? 2 : 4); }
 
-// gate/up: grid.x = max_chunks * (I / 64)
+// LDS bytes of one class: x staging, z rows (up to 2 blocks x 128 columns),
+// per-wave LUTs (bit-plane: 2 streams per wave).
+inline size_t stream_lds_bytes(bool plane, int nsub) {
+  size_t b = (size_t)nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 256 * 2;
+  if (plane) b += (size_t)4 * 2 * kLutBlk * 2;
+  return b;
+}
+
+template <int NSUB>
+__device__ __forceinline__ uint16_t *lut_region(uint16_t *lds, int wave) {
+  return lds + NSUB * 16 * kXStride + NSUB * 16 * 256 + wave * 2 * kLutBlk;
+}
+
+// gate/up: 256 threads; grid.x = max_chunks * (I / 64)
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 2) gateup_kernel(FfnArgs a) {
-  uint16_t *xs = dyn_lds();
-  const int wave = threadIdx.x >> 6;
-  const int n_sg = a.I / (16 * kStripsPerWG);
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 2 : 1)) gateup_kernel(FfnArgs a) {
+  uint16_t *lds = dyn_lds();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_sg = a.I / 64;
   const int chunk = blockIdx.x / n_sg, sg = blockIdx.x % n_sg;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
-  const int strip = sg * kStripsPerWG + wave;
-  uint16_t *ll = xs + NSUB * 16 * kXStride + (PLANE ? wave * 2 * kLutBlk : 0);
+  const int strip = 4 * sg + wave;
+  uint16_t *ll = lut_region<NSUB>(lds, wave);
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
-    case 2 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 2, 2>(a, ch, strip, xs, ll); break;
-    case 2 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 2, 3>(a, ch, strip, xs, ll); break;
-    case 2 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 2, 4>(a, ch, strip, xs, ll); break;
-    case 3 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 3, 2>(a, ch, strip, xs, ll); break;
-    case 3 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 3, 3>(a, ch, strip, xs, ll); break;
-    case 3 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 3, 4>(a, ch, strip, xs, ll); break;
-    case 4 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 4, 2>(a, ch, strip, xs, ll); break;
-    case 4 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 4, 3>(a, ch, strip, xs, ll); break;
-    default: gateup_body<NSUB, GPT, PLANE, 4, 4>(a, ch, strip, xs, ll); break;
+    case 2 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 2, 2>(a, ch, strip, lds, ll); break;
+    case 2 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 2, 3>(a, ch, strip, lds, ll); break;
+    case 2 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 2, 4>(a, ch, strip, lds, ll); break;
+    case 3 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 3, 2>(a, ch, strip, lds, ll); break;
+    case 3 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 3, 3>(a, ch, strip, lds, ll); break;
+    case 3 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 3, 4>(a, ch, strip, lds, ll); break;
+    case 4 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 4, 2>(a, ch, strip, lds, ll); break;
+    case 4 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 4, 3>(a, ch, strip, lds, ll); break;
+    default: gateup_body<NSUB, GPT, PLANE, 4, 4>(a, ch, strip, lds, ll); break;
   }
 }
 
-// down: grid.x = max_chunks * (H / 64) * splits
+// down: 256 threads, 128 rows; grid.x = max_chunks * (H / 128) * splits
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 2) down_kernel(FfnArgs a) {
-  uint16_t *xs = dyn_lds();
-  const int wave = threadIdx.x >> 6;
-  const int n_sg = a.H / (16 * kStripsPerWG);
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 2 : 1)) down_kernel(FfnArgs a) {
+  uint16_t *lds = dyn_lds();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_sg = a.H / 128;
   const int split = blockIdx.x % a.splits;
   const int rest = blockIdx.x / a.splits;
   const int chunk = rest / n_sg, sg = rest % n_sg;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
-  const int strip = sg * kStripsPerWG + wave;
-  uint16_t *ll = xs + NSUB * 16 * kXStride + (PLANE ? wave * kLutBlk : 0);
+  uint16_t *ll = lut_region<NSUB>(lds, wave);
   switch (a.desc[3 * ch.e + 2].bits) {
-    case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, strip, split, xs, ll); break;
-    case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, strip, split, xs, ll); break;
-    default: down_body<NSUB, GPT, PLANE, 4>(a, ch, strip, split, xs, ll); break;
+    case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, sg, split, lds, ll); break;
+    case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, sg, split, lds, ll); break;
+    default: down_body<NSUB, GPT, PLANE, 4>(a, ch, sg, split, lds, ll); break;
   }
-}
-
-inline size_t stream_lds_bytes(bool plane, int nsub, int nb) {
-  size_t b = (size_t)nsub * 16 * kXStride * 2;
-  if (plane) b += (size_t)4 * nb * kLutBlk * 2;
-  return b;
 }
 
 // Launch helpers for one (GPT, PLANE) class, instantiated in the .hip files.
 template <int GPT, bool PLANE>
 void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, 2), s, a);
+  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1), s, a);
   if (a.nsub_max >= 2)
-    hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, 2), s, a);
+    hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2), s, a);
   if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, 2), s, a);
+    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4), s, a);
 }
 
 template <int GPT, bool PLANE>
 void launch_down_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, 1), s, a);
+  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1), s, a);
   if (a.nsub_max >= 2)
-    hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, 1), s, a);
+    hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2), s, a);
   if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, 1), s, a);
+    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4), s, a);
 }
 
 void launch_gateup_g128(const FfnArgs &a, int grid, hipStream_t s);
