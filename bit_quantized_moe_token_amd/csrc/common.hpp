@@ -65,6 +65,13 @@ __device__ __forceinline__ T gld(const void *p) {
   return *(const __attribute__((address_space(1))) T *)(p);
 }
 
+// Non-temporal global load: for data read once per call (packed weights),
+// so that it streams past the caches instead of displacing reused data.
+template <typename T>
+__device__ __forceinline__ T gld_nt(const void *p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)(p));
+}
+
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return (a & m) | c;   // v_and_or_b32
 }

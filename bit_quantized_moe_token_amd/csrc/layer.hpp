@@ -12,12 +12,30 @@ __host__ __device__ inline int lane_tile_bytes(int fmt, int bits) {
 
 // Byte offset of lane l's data for tile t of strip s in a code region whose
 // lanes hold W bytes per tile.  Tiles are grouped by four; inside a group a
-// lane's bytes for the group's tiles are contiguous.
+// lane's bytes for the group's tiles are contiguous.  (Bit-plane regions,
+// W = 4: one 16-byte chunk per lane per full group.)
 __host__ __device__ inline uint64_t code_offset(int s, int t, int l, int n_kt, int W) {
   const int g4 = t >> 2, tl = t & 3;
   const int c = (n_kt - 4 * g4) < 4 ? (n_kt - 4 * g4) : 4;
   return (uint64_t)s * n_kt * 64 * W + (uint64_t)g4 * 256 * W + (uint64_t)l * c * W +
          (uint64_t)tl * W;
+}
+
+// Byte offset of dword e (0 <= e < B) of tile t, lane l, strip s of an INT
+// code region (B dwords per lane per tile).  In a full group of four tiles
+// the lane's 4*B dwords d = 4*tl... are split into B 16-byte chunks
+// (dwords 4i..4i+3, d = tl*B + e) and chunk i of all 64 lanes is
+// contiguous, so every 128-bit load instruction of a wave reads 1 KiB of
+// consecutive bytes.  A ragged last group keeps the lane-contiguous layout.
+__host__ __device__ inline uint64_t int_word_offset(int s, int t, int l, int e, int n_kt, int B) {
+  const int g4 = t >> 2, tl = t & 3;
+  const int c = (n_kt - 4 * g4) < 4 ? (n_kt - 4 * g4) : 4;
+  const uint64_t base = (uint64_t)s * n_kt * 256 * B + (uint64_t)g4 * 1024 * B;
+  if (c == 4) {
+    const int d = tl * B + e;
+    return base + (uint64_t)((d >> 2) * 64 + l) * 16 + (d & 3) * 4;
+  }
+  return base + (uint64_t)l * c * 4 * B + (uint64_t)tl * 4 * B + e * 4;
 }
 
 // Element index of the scale / zero of (strip s, tile t, row r, group gi in

@@ -55,9 +55,8 @@ pack_int_kernel(const uint8_t *__restrict__ codes, int N, int K, uint8_t *__rest
       }
     }
   }
-  uint32_t *dst = reinterpret_cast<uint32_t *>(out + code_offset(s, t, l, n_kt, 4 * B));
 #pragma unroll
-  for (int e = 0; e < B; ++e) dst[e] = d[e];
+  for (int e = 0; e < B; ++e) *reinterpret_cast<uint32_t *>(out + int_word_offset(s, t, l, e, n_kt, B)) = d[e];
 }
 
 // Four bit-planes of 4-bit parent codes; plane c goes to region 3 - c.
@@ -126,10 +125,9 @@ unpack_int_kernel(const uint8_t *__restrict__ packed, int N, int K, uint8_t *__r
   const int l = (int)(id & 63);
   const int t = (int)((id >> 6) % n_kt);
   const int s = (int)((id >> 6) / n_kt);
-  const uint32_t *src = reinterpret_cast<const uint32_t *>(packed + code_offset(s, t, l, n_kt, 4 * B));
   uint32_t d[B];
 #pragma unroll
-  for (int e = 0; e < B; ++e) d[e] = src[e];
+  for (int e = 0; e < B; ++e) d[e] = *reinterpret_cast<const uint32_t *>(packed + int_word_offset(s, t, l, e, n_kt, B));
   PairConst pc[9];
   fill_pair_consts<B>(pc, 0.0f);
   uint8_t *dst = out + (int64_t)(s * kStripRows + (l & 15)) * K;

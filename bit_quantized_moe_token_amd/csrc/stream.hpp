@@ -45,11 +45,12 @@ struct Group {
 template <int B, int C, int GPT>
 __device__ __forceinline__ void load_int_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, false> &g) {
   const int lane = threadIdx.x & 63, r = lane & 15;
-  const uint8_t *p = d.codes + code_offset(strip, 4 * g4, lane, n_kt, 4 * B);
+  const uint8_t *p = d.codes + int_word_offset(strip, 4 * g4, lane, 0, n_kt, B);
   if (C == 4) {
+    // chunk i of the group: 1 KiB of consecutive bytes across the wave
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const u32x4 v = gld<u32x4>(p + 16 * i);
+      const u32x4 v = gld_nt<u32x4>(p + 1024 * i);
       g.w[4 * i] = v[0]; g.w[4 * i + 1] = v[1]; g.w[4 * i + 2] = v[2]; g.w[4 * i + 3] = v[3];
     }
   } else {
