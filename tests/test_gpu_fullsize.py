@@ -1,0 +1,58 @@
+"""GPU parity at the full Mixtral-shaped sizes (H 4096, I 14336, 8 experts,
+top-2) in the launch configuration the benchmark times: the whole layer is
+quantized and packed by the library, routed and evaluated for the whole
+batch, and the oracle recomputes sampled outputs one by one (every gate/up
+row of the sampled tokens' experts, the down rows of the sampled output
+columns) from its own quantization of the same fp16 weights."""
+
+import numpy as np
+import pytest
+
+from synth import configs, gen
+from tests import layers
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _sample_cols(H, n, seed):
+    rng = np.random.default_rng([seed, 99])
+    cols = set(rng.choice(H, size=n, replace=False).tolist())
+    cols |= {0, 1, 127, 128, H - 129, H - 1}          # first/last tiles and strip edges
+    return np.array(sorted(cols))
+
+
+def _run_full(name, tokens, n_cols, seed=0):
+    from bit_quantized_moe_token_amd import moeq
+    cfg = configs.get(name)
+    x = gen.gen_x(cfg, seed)
+    logits = gen.gen_logits(cfg, seed)
+    dev = layers.device_layer(cfg, seed)
+    xd = torch.from_numpy(x).cuda()
+    rt = moeq.route(torch.from_numpy(logits).cuda(), cfg["k"])
+    y = moeq.expert_ffn(dev, xd, rt, cfg["n_comp"], out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    del dev
+    torch.cuda.empty_cache()
+    cols = _sample_cols(cfg["H"], n_cols, seed)
+    orc = layers.oracle_layer(cfg, seed, cache_blocks=2 * cfg["E"])
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"], tokens=tokens, cols=cols)
+    rel, fro = layers.check_y(y[np.ix_(tokens, cols)], ref, name)
+    print(f"{name} full size, {len(tokens)} tokens x {len(cols)} columns: "
+          f"max|err|/rms {rel:.2e}  fro {fro:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_decode_full_size_sampled():
+    """Mixtral decode: 16 tokens, int3 G128, rank 32 (all tokens checked)."""
+    _run_full("decode", np.arange(16), 384)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_full_size_sampled():
+    """Mixtral prefill: 4096 tokens, int4 G128, rank 32; tokens sampled
+    across the batch, including the first and the last."""
+    T = configs.get("prefill")["T"]
+    tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 7).astype(int)]))
+    _run_full("prefill", tokens, 256)
