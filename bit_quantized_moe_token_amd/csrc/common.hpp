@@ -72,8 +72,14 @@ __device__ __forceinline__ T gld_nt(const void *p) {
   return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)(p));
 }
 
+// (a & m) | c as one v_and_or_b32.  A VOP3 instruction on this target
+// takes no literal operand, so with literal m and c the compiler would emit
+// a v_and_b32 and a v_or_b32; the asm operands make it keep the constants
+// in registers (hoisted out of loops) and issue the single instruction.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  return (a & m) | c;   // v_and_or_b32
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }

@@ -16,7 +16,29 @@ struct Ws {
   int ks_gu, ks_d;
 };
 
+// Kernel path of one call.  Tiled: INT blocks, on average >= 64 pairs per
+// expert, shapes the tiled kernels cover (H a multiple of 256, 32-bit
+// element offsets of the activation rows, z rows that fit one activation
+// buffer); weight streaming otherwise.
+static bool tiled_fits(const moeq_layer *L, int T, int k) {
+  const LayerDims &D = L->dims;
+  const int64_t P = (int64_t)T * k;
+  const int RZ = (D.r + 31) / 32 * 32 + (D.rs + 31) / 32 * 32;
+  return D.fmt == MOEQ_FMT_INT && D.H % 256 == 0 && D.I % kTileK == 0 &&
+         (int64_t)T * D.H < (1ll << 31) && P * D.I < (1ll << 31) && 2 * RZ <= kTileK + 8;
+}
+
+static int pick_path(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
+  const int want = o ? o->path : MOEQ_PATH_AUTO;
+  if (want == MOEQ_PATH_TILED) return tiled_fits(L, T, k) ? MOEQ_PATH_TILED : -1;
+  if (want == MOEQ_PATH_STREAM) return MOEQ_PATH_STREAM;
+  if (want != MOEQ_PATH_AUTO) return -1;
+  const int64_t P = (int64_t)T * k;
+  return (tiled_fits(L, T, k) && P >= 64ll * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
+}
+
 static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
+  if (pick_path(L, T, k, o) == MOEQ_PATH_TILED) return 1;
   if (o && o->split_k > 0) return o->split_k;
   const int P = T * k;
   const int n_g4 = (L->dims.I / kTileK + 3) / 4;
@@ -70,9 +92,10 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   if (T < 0 || k < 1 || k > D.E) return fail(MOEQ_ERR_INVALID, "expert_ffn: T=%d k=%d invalid for E=%d", T, k, D.E);
   if (n_comp < 0 || n_comp > k) return fail(MOEQ_ERR_INVALID, "expert_ffn: n_comp=%d not in 0..%d", n_comp, k);
   if (y_dtype != MOEQ_F16 && y_dtype != MOEQ_F32) return fail(MOEQ_ERR_INVALID, "expert_ffn: bad y_dtype %d", y_dtype);
-  const int path = opts ? opts->path : MOEQ_PATH_AUTO;
-  if (path != MOEQ_PATH_AUTO && path != MOEQ_PATH_STREAM)
-    return fail(MOEQ_ERR_UNSUPPORTED, "expert_ffn: path %d not available", path);
+  const int path = pick_path(L, T, k, opts);
+  if (path < 0)
+    return fail(MOEQ_ERR_UNSUPPORTED, "expert_ffn: path %d not available for this layer and batch",
+                opts ? opts->path : 0);
   if (opts && (opts->split_k < 0 || opts->split_k > 64)) return fail(MOEQ_ERR_INVALID, "expert_ffn: split_k=%d not in 0..64", opts->split_k);
   if (T == 0) return MOEQ_OK;
   if (!x || !y || !r->topk_gates || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
@@ -114,17 +137,31 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
     launch_lowrank_project(a, 0, dim3(mc * 4, 2 * a.RZ / 16), stream);
     prof_end("lowrank_project_gu", stream);
   }
-  prof_begin("gateup_stream", stream);
-  launch_gateup_stream(a, mc * (D.I / 64), stream);
-  prof_end("gateup_stream", stream);
+  const bool tiled = path == MOEQ_PATH_TILED;
+  const int mt = tiled ? max_chunks(D.E, T, k, kTiledM) : 0;     // token tiles of the tiled path
+  if (tiled) {
+    prof_begin("gateup_tiled", stream);
+    launch_tiled_gateup(a, (mt * (D.I / kTileK) + 7) / 8 * 8, stream);
+    prof_end("gateup_tiled", stream);
+  } else {
+    prof_begin("gateup_stream", stream);
+    launch_gateup_stream(a, mc * (D.I / 64), stream);
+    prof_end("gateup_stream", stream);
+  }
   if (a.comp_on) {
     prof_begin("lowrank_project_down", stream);
     launch_lowrank_project(a, 1, dim3(mc * 4, a.RZ / 16), stream);
     prof_end("lowrank_project_down", stream);
   }
-  prof_begin("down_stream", stream);
-  launch_down_stream(a, mc * (D.H / 128) * splits, stream);
-  prof_end("down_stream", stream);
+  if (tiled) {
+    prof_begin("down_tiled", stream);
+    launch_tiled_down(a, (mt * (D.H / 256) + 7) / 8 * 8, stream);
+    prof_end("down_tiled", stream);
+  } else {
+    prof_begin("down_stream", stream);
+    launch_down_stream(a, mc * (D.H / 128) * splits, stream);
+    prof_end("down_stream", stream);
+  }
   prof_begin("combine", stream);
   launch_combine(a, y, y_dtype == MOEQ_F32, stream);
   prof_end("combine", stream);

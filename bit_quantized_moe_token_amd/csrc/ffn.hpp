@@ -7,6 +7,7 @@
 namespace moeq {
 
 constexpr int kMT = 64;            // tokens per chunk (up to four 16-row MFMA tiles)
+constexpr int kTiledM = 128;       // tokens per token tile of the tiled kernels
 constexpr int kStripsPerWG = 4;    // one 16-row strip per wave
 
 struct FfnArgs {
@@ -36,15 +37,16 @@ struct Chunk {
 };
 
 // Chunk c of the expert-major chunk list (each expert's tokens cut into
-// pieces of kMT): expert, first token within the expert, token count and
+// pieces of MT): expert, first token within the expert, token count and
 // first sorted position.  Wave-uniform; false when c is past the end.
+template <int MT = kMT>
 __device__ __forceinline__ bool find_chunk(const int32_t *__restrict__ off, int E, int c, Chunk *out) {
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int b = 0; b < E; b += kWave) {
     const int e = b + lane;
     const int cnt = e < E ? off[e + 1] - off[e] : 0;
-    const int nc = (cnt + kMT - 1) / kMT;
+    const int nc = (cnt + MT - 1) / MT;
     int incl = nc;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -60,8 +62,8 @@ __device__ __forceinline__ bool find_chunk(const int32_t *__restrict__ off, int 
       const int ex = __builtin_amdgcn_readfirstlane(__shfl(excl, src, kWave));
       const int cn = __builtin_amdgcn_readfirstlane(__shfl(cnt, src, kWave));
       out->e = __builtin_amdgcn_readfirstlane(b + src);
-      out->m0 = (c - ex) * kMT;
-      out->cnt = std::min(kMT, cn - out->m0);
+      out->m0 = (c - ex) * MT;
+      out->cnt = std::min(MT, cn - out->m0);
       out->base = off[out->e] + out->m0;
       return true;
     }
@@ -79,12 +81,13 @@ __device__ __forceinline__ f16x8 pack_b(uint32_t a, uint32_t b, uint32_t c, uint
   return __builtin_bit_cast(f16x8, v);
 }
 
-// Upper bound of the number of chunks for T tokens, top-k, E experts.
-inline int max_chunks(int E, int T, int k) {
+// Upper bound of the number of chunks of MT pairs for T tokens, top-k, E
+// experts (an expert holds at most T pairs).
+inline int max_chunks(int E, int T, int k, int MT = kMT) {
   const int64_t P = (int64_t)T * k;
-  const int64_t a = (int64_t)E * ((T + kMT - 1) / kMT);
+  const int64_t a = (int64_t)E * ((T + MT - 1) / MT);
   const int64_t act = std::min<int64_t>(E, P);
-  const int64_t b = (P + act * (kMT - 1)) / kMT;
+  const int64_t b = (P + act * (MT - 1)) / MT;
   return (int)std::max<int64_t>(0, std::min(a, b));
 }
 
@@ -93,5 +96,7 @@ void launch_gateup_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_down_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s);
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s);
+void launch_tiled_gateup(const FfnArgs &a, int grid, hipStream_t s);   // tiled_gu.hip
+void launch_tiled_down(const FfnArgs &a, int grid, hipStream_t s);     // tiled_dn.hip
 
 }  // namespace moeq

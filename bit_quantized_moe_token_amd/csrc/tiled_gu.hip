@@ -1,0 +1,13 @@
+// Instantiation of the tiled gate/up kernels (see tiled.hpp).
+#include "tiled.hpp"
+
+namespace moeq {
+
+void launch_tiled_gateup(const FfnArgs &a, int grid, hipStream_t s) {
+  if (a.G == 64)
+    hipLaunchKernelGGL((tiled_gateup_kernel<2, kTiledWaves>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL((tiled_gateup_kernel<1, kTiledWaves>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
+}
+
+}  // namespace moeq

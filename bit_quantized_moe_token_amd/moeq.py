@@ -11,7 +11,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import check, lib
+from ._lib import MoeqError, check, lib  # noqa: F401
 
 GATE, UP, DOWN = 0, 1, 2
 
@@ -177,6 +177,10 @@ class RoutingOut:
         self.pair_pos = torch.empty((P,), dtype=torch.int32, device=device)
         self.c = _lib.Routing(self.ids.data_ptr(), self.gates.data_ptr(), self.offsets.data_ptr(),
                               self.sorted_pairs.data_ptr(), self.pair_pos.data_ptr())
+        n = ctypes.c_size_t(0)
+        check(lib().moeq_route_workspace_size(T, E, k, ctypes.byref(n)), "moeq_route_workspace_size")
+        self.ws = torch.empty((max(1, n.value),), dtype=torch.uint8, device=device)
+        self.ws_bytes = n.value
 
 
 def route(logits, k, out=None):
@@ -185,7 +189,8 @@ def route(logits, k, out=None):
     _need(logits, torch.float32, (T, E), "logits")
     if out is None:
         out = RoutingOut(T, E, k, logits.device)
-    check(lib().moeq_route(_ptr(logits), T, E, k, ctypes.byref(out.c), None, 0, _stream()), "moeq_route")
+    check(lib().moeq_route(_ptr(logits), T, E, k, ctypes.byref(out.c), _ptr(out.ws), out.ws_bytes, _stream()),
+          "moeq_route")
     return out
 
 

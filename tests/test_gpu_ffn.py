@@ -39,11 +39,14 @@ def _setup(case, seed=0):
     return _cache[key]
 
 
-def _run(dev, cfg, x, logits, n_comp, out_dtype=torch.float16, split_k=0):
+PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 3
+
+
+def _run(dev, cfg, x, logits, n_comp, out_dtype=torch.float16, split_k=0, path=PATH_AUTO):
     from bit_quantized_moe_token_amd import moeq
     xd = torch.from_numpy(x).cuda()
     rt = moeq.route(torch.from_numpy(logits).cuda(), cfg["k"])
-    y = moeq.expert_ffn(dev, xd, rt, n_comp, out_dtype=out_dtype, split_k=split_k)
+    y = moeq.expert_ffn(dev, xd, rt, n_comp, out_dtype=out_dtype, split_k=split_k, path=path)
     torch.cuda.synchronize()
     return y
 
@@ -115,3 +118,41 @@ def test_ffn_zero_input_and_few_tokens():
         sub = dict(cfg, T=T)
         y = _run(dev, sub, x[:T].copy(), logits[:T].copy(), cfg["k"], out_dtype=torch.float32)
         layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, sub, x[:T], logits[:T], cfg["k"]), f"T={T}")
+
+
+# ---- tiled path (many tokens per expert): forced on every INT workload,
+# including one token tile per expert (decode), mixed 2/3/4-bit blocks with
+# group 64 and an odd, ragged K-tile count (fine-grained: I = 1408 = 11 tiles)
+
+@pytest.mark.parametrize("case", ["tiny", "decode", "prefill", "finegrained"])
+def test_ffn_tiled_path_matches_oracle(case):
+    cfg, orc, dev, x, logits = _setup(case)
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
+    y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
+    rel, fro = layers.check_y(y.cpu().numpy(), ref, case + " tiled")
+    print(f"{case} tiled: max|err|/rms {rel:.2e}  fro {fro:.2e}")
+    y0 = _run(dev, cfg, x, logits, 0, out_dtype=torch.float32, path=PATH_TILED)
+    layers.check_y(y0.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, 0), case + " tiled n_comp=0")
+
+
+def test_ffn_prefill_paths():
+    """The batch of the prefill workload takes the tiled path by default;
+    the streaming path gives the same result within the tolerance."""
+    cfg, orc, dev, x, logits = _setup("prefill")
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
+    auto = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    tiled = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
+    assert torch.equal(auto, tiled)
+    stream = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
+    layers.check_y(stream.cpu().numpy(), ref, "prefill stream")
+    perm = np.random.default_rng(7).permutation(cfg["T"])
+    tp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32,
+              path=PATH_TILED)
+    assert torch.equal(tp, tiled[torch.from_numpy(perm).cuda()])
+
+
+def test_ffn_tiled_unsupported_for_bitplane():
+    from bit_quantized_moe_token_amd import moeq
+    cfg, orc, dev, x, logits = _setup("bitplane")
+    with pytest.raises(moeq.MoeqError):
+        _run(dev, cfg, x, logits, cfg["n_comp"], path=PATH_TILED)

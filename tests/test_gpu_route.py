@@ -30,7 +30,9 @@ def _check(logits, k):
     assert np.array_equal(rt.pair_pos.cpu().numpy(), ref["pair_pos"])
     g = rt.gates.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(g - ref["gates"])) <= 2e-6
-    assert np.max(np.abs(g.sum(1) - 1)) <= 2e-6
+    # the kernel's softmax denominator is an fp32 sum of k terms, so the k
+    # fp32 gates sum to 1 within about k units of 2^-24 (k + 4 ulp of 1 here)
+    assert np.max(np.abs(g.sum(1) - 1)) <= max(2e-6, (k + 4) * 2.0 ** -23)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "finegrained", "bitplane"])
@@ -41,7 +43,8 @@ def test_route_configs(name, seed):
 
 
 @pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 8), (5, 3, 1), (333, 256, 7), (70, 64, 64),
-                                   (2000, 5, 2), (1030, 128, 8), (4096, 2, 2)])
+                                   (2000, 5, 2), (1030, 128, 8), (4096, 2, 2), (64, 8, 2), (65, 256, 256),
+                                   (129, 7, 3)])
 def test_route_shapes_and_ties(T, E, k):
     rng = np.random.default_rng(T + E + k)
     logits = (rng.integers(-2, 3, size=(T, E)) * 0.25).astype(np.float32)   # many ties
