@@ -50,6 +50,7 @@ def parse():
                    default="decode")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--path", type=int, default=0, help="moeq_path (0 = auto)")
+    p.add_argument("--split-k", type=int, default=0, help="down-projection K splits (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
@@ -58,6 +59,8 @@ def parse():
                         "WRITE_SIZE) of a --copy-calibration run and record the scaled "
                         "per-launch HBM traffic of each kernel of the workload")
     p.add_argument("--no-extra", action="store_true", help="skip the extra prefill measurement")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step from a captured HIP graph instead of launching it directly")
     return p.parse_args()
 
 
@@ -163,7 +166,7 @@ def time_steps(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
-def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True):
+def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, graph=False, split_k=0):
     import numpy as np
     import torch
     from bit_quantized_moe_token_amd import moeq
@@ -174,14 +177,32 @@ def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True):
     logits = torch.from_numpy(gen.gen_logits(cfg, seed)).cuda()
     rt = moeq.RoutingOut(T, cfg["E"], k, x.device)
     y = torch.empty((T, cfg["H"]), dtype=torch.float16, device=x.device)
-    ws = moeq.FfnWorkspace(layers_list[0], T, k, path)
+    ws = moeq.FfnWorkspace(layers_list[0], T, k, path, split_k)
     R = len(layers_list)
 
     def step(i):
         moeq.route(logits, k, out=rt)
-        moeq.expert_ffn(layers_list[i % R], x, rt, cfg["n_comp"], out=y, ws=ws, path=path)
+        moeq.expert_ffn(layers_list[i % R], x, rt, cfg["n_comp"], out=y, ws=ws, path=path, split_k=split_k)
 
-    ms = time_steps(step, steps, warmup)
+    timed = step
+    if graph:
+        # one HIP graph per weight copy holding the step's launches (the
+        # library's calls enqueue kernels only: no host syncs, no memsets)
+        for i in range(R):
+            step(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def timed(i):
+            graphs[i % R].replay()
+
+    ms = time_steps(timed, steps, warmup)
     prof = {}
     if profile:
         moeq.profile_enable(True)
@@ -342,7 +363,8 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
-    ms, prof, alg = run_workload(cfg, layers["main"], args.seed, args.steps, args.warmup, args.path)
+    ms, prof, alg = run_workload(cfg, layers["main"], args.seed, args.steps, args.warmup, args.path,
+                                 graph=args.graph, split_k=args.split_k)
     T = cfg["T"]
     tokens_s = T / (ms * 1e-3)
 
@@ -375,7 +397,8 @@ def main():
         "config": {"workload": cfg["name"], "T": T, "E": cfg["E"], "k": cfg["k"], "H": cfg["H"],
                    "I": cfg["I"], "fmt": cfg["fmt"], "bits": cfg["bits"], "G": cfg["G"],
                    "r": cfg["r"], "n_comp": cfg["n_comp"], "seed": args.seed,
-                   "weight_copies": copies["main"], "parallelism": "none (1 GPU)"},
+                   "weight_copies": copies["main"], "parallelism": "none (1 GPU)",
+                   "launch": "hip_graph" if args.graph else "stream"},
         "roofline": roofline,
         "layer": dict(alg_bytes=alg["bytes"], alg_flops=alg["flops"], active_experts=alg["active"],
                       expert_counts=alg["counts"],
@@ -386,7 +409,7 @@ def main():
     }
     if extra_cfg is not None:
         pms, pprof, palg = run_workload(extra_cfg, layers["prefill"], args.seed, max(3, args.steps // 20),
-                                        max(1, args.warmup // 10), args.path)
+                                        max(1, args.warmup // 10), args.path, graph=args.graph)
         pk = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in pprof.items()}
         out["prefill"] = dict(workload=extra_cfg["name"], ms_per_step=pms,
                               tokens_s=extra_cfg["T"] / (pms * 1e-3), alg_flops=palg["flops"],

@@ -66,18 +66,25 @@ __device__ __forceinline__ constexpr int int_pair_shift(int P) {
 }
 
 // Per-(row, group) constants turning a biased pair into (c - z) exactly:
-// (1024 + c 2^p) * 2^-p - (1024 * 2^-p + z) = c - z.
+// (1024 + c 2^p) * 2^-p - (1024 * 2^-p + z) = c - z.  The fp16 constant
+// -(2^(10-p) + z) is built from the integer zero directly: exponent field
+// 25 - p and mantissa z * 2^p (exact while z * 2^p < 1024, which holds for
+// every field of the b-bit layouts: z < 2^b, p <= 10 - b).  With the zero
+// duplicated into both halves once per group, each constant is one
+// shift-or.
 struct PairConst {
-  f16x2 mul, add;
+  uint32_t add;   // fp16 pair -(2^(10-p) + z)
 };
-__device__ __forceinline__ PairConst pair_const(int p, float z) {
-  const float inv = __builtin_ldexpf(1.0f, -p);
-  const f16 m = (f16)inv;
-  const f16 a = (f16)(-(1024.0f * inv + z));
-  PairConst c;
-  c.mul = f16x2{m, m};
-  c.add = f16x2{a, a};
-  return c;
+
+__device__ __forceinline__ constexpr uint32_t pair_add_base(int p) {
+  return (0x8000u | ((uint32_t)(25 - p) << 10)) * 0x10001u;
+}
+
+// 2^-p as an fp16 pair (p is a constant after unrolling).
+__device__ __forceinline__ f16x2 pair_mul(int p) {
+  const f16 m = (f16)(p == 2 ? 0.25f : p == 3 ? 0.125f : p == 4 ? 0.0625f : p == 6 ? 0.015625f
+                      : p == 8 ? 0.00390625f : 1.0f);
+  return f16x2{m, m};
 }
 
 __device__ __forceinline__ f16x2 pk_fma(f16x2 a, f16x2 b, f16x2 c) {
@@ -85,14 +92,20 @@ __device__ __forceinline__ f16x2 pk_fma(f16x2 a, f16x2 b, f16x2 c) {
 }
 
 // Pair constants for every field scale a b-bit tile uses (indexed by the
-// field's bit offset p; unused slots are left untouched).
+// field's bit offset p; unused slots are left untouched); z is the integer
+// zero of the group.
 template <int B>
-__device__ __forceinline__ void fill_pair_consts(PairConst *pc, float z) {
-  if (B == 4) { pc[0] = pair_const(0, z); pc[4] = pair_const(4, z); }
-  if (B == 3) { pc[0] = pair_const(0, z); pc[3] = pair_const(3, z); pc[6] = pair_const(6, z); }
+__device__ __forceinline__ void fill_pair_consts(PairConst *pc, uint32_t z) {
+  const uint32_t z2 = z | (z << 16);
+  if (B == 4) { pc[0].add = z2 | pair_add_base(0); pc[4].add = (z2 << 4) | pair_add_base(4); }
+  if (B == 3) {
+    pc[0].add = z2 | pair_add_base(0); pc[3].add = (z2 << 3) | pair_add_base(3);
+    pc[6].add = (z2 << 6) | pair_add_base(6);
+  }
   if (B == 2) {
-    pc[0] = pair_const(0, z); pc[2] = pair_const(2, z); pc[4] = pair_const(4, z);
-    pc[6] = pair_const(6, z); pc[8] = pair_const(8, z);
+    pc[0].add = z2 | pair_add_base(0); pc[2].add = (z2 << 2) | pair_add_base(2);
+    pc[4].add = (z2 << 4) | pair_add_base(4); pc[6].add = (z2 << 6) | pair_add_base(6);
+    pc[8].add = (z2 << 8) | pair_add_base(8);
   }
 }
 
@@ -102,7 +115,8 @@ template <int B>
 __device__ __forceinline__ uint32_t int_pair_cz(const uint32_t *d, int P, const PairConst *pc) {
   const uint32_t raw = int_pair_raw<B>(d, P);
   const int p = int_pair_shift<B>(P);
-  return as_u32(pk_fma(as_h2(raw), pc[p].mul, pc[p].add));
+  if (p == 0) return as_u32(as_h2(raw) + as_h2(pc[0].add));
+  return as_u32(pk_fma(as_h2(raw), pair_mul(p), as_h2(pc[p].add)));
 }
 
 // Merged q-bit indices of MFMA step j from the top q planes (pl[0] = plane

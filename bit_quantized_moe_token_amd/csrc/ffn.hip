@@ -43,7 +43,7 @@ static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options
   const int P = T * k;
   const int n_g4 = (L->dims.I / kTileK + 3) / 4;
   // few tokens: split the long down-projection K for more waves in flight
-  int s = P <= 256 ? 8 : 1;
+  int s = P <= 256 ? 4 : 1;
   return std::max(1, std::min(s, n_g4));
 }
 

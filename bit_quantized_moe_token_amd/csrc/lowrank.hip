@@ -45,11 +45,29 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const int nsteps = K / 32;
   const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
   const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int st = s0; st < s1; ++st) {
-    f16x8 b = vi ? load_a(vrow + 32 * st) : pack_b(0, 0, 0, 0);
+  // batches of 8 steps: all 16 fragment loads are issued before the first
+  // MFMA, so each batch waits for memory once
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+  int st = s0;
+  for (; st + 8 <= s1; st += 8) {
+    f16x8 av[8], bv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      av[u] = load_a(arow + 32 * (st + u));
+      bv[u] = vi ? load_a(vrow + 32 * (st + u)) : pack_b(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      acc = mfma16(av[u], bv[u], acc);
+      acc2 = mfma16(av[u + 1], bv[u + 1], acc2);
+    }
+  }
+  for (; st < s1; ++st) {
+    const f16x8 b = vi ? load_a(vrow + 32 * st) : pack_b(0, 0, 0, 0);
     acc = mfma16(load_a(arow + 32 * st), b, acc);
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] += acc2[q];
   s_part[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;

@@ -129,7 +129,7 @@ unpack_int_kernel(const uint8_t *__restrict__ packed, int N, int K, uint8_t *__r
 #pragma unroll
   for (int e = 0; e < B; ++e) d[e] = *reinterpret_cast<const uint32_t *>(packed + int_word_offset(s, t, l, e, n_kt, B));
   PairConst pc[9];
-  fill_pair_consts<B>(pc, 0.0f);
+  fill_pair_consts<B>(pc, 0u);
   uint8_t *dst = out + (int64_t)(s * kStripRows + (l & 15)) * K;
 #pragma unroll
   for (int P = 0; P < 16; ++P) {

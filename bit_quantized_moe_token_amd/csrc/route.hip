@@ -168,19 +168,19 @@ constexpr int kSegThreads = 256;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kSegTokens = 64;
 
-// Segment blockIdx.x: top-k of its tokens (one wave per token) and its
-// per-expert pair counts seg_count[seg][e].
-__global__ void __launch_bounds__(kSegThreads)
+// Segment blockIdx.x: top-k of its tokens (16 waves, one per token) and
+// its per-expert pair counts seg_count[seg][e].
+__global__ void __launch_bounds__(kRouteThreads)
 route_topk_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
                   float *__restrict__ gates, int32_t *__restrict__ seg_count) {
   __shared__ int s_hist[kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int e = tid; e < kMaxE; e += kSegThreads) s_hist[e] = 0;
+  for (int e = tid; e < kMaxE; e += kRouteThreads) s_hist[e] = 0;
   __syncthreads();
   const int t0 = blockIdx.x * kSegTokens, t1 = std::min(T, t0 + kSegTokens);
-  for (int t = t0 + wave; t < t1; t += kSegWaves) topk_token(logits, t, E, k, ids, gates, s_hist);
+  for (int t = t0 + wave; t < t1; t += kRouteWaves) topk_token(logits, t, E, k, ids, gates, s_hist);
   __syncthreads();
-  for (int e = tid; e < E; e += kSegThreads) seg_count[(int64_t)blockIdx.x * E + e] = s_hist[e];
+  for (int e = tid; e < E; e += kRouteThreads) seg_count[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
 // Segment blockIdx.x: expert offsets from every segment's counts (segment 0
@@ -201,6 +201,7 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, const i
   const int seg = blockIdx.x;
   for (int e = tid; e < E; e += kSegThreads) {
     int tot = 0, before = 0;
+#pragma unroll 8
     for (int g = 0; g < nseg; ++g) {
       const int c = seg_count[(int64_t)g * E + e];
       tot += c;
@@ -309,7 +310,7 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
                        out->pair_pos);
   } else {
     int32_t *cnt = static_cast<int32_t *>(ws);
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nseg), dim3(kSegThreads), 0, stream, logits, T, E, k,
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nseg), dim3(kRouteThreads), 0, stream, logits, T, E, k,
                        out->topk_ids, out->topk_gates, cnt);
     hipLaunchKernelGGL(route_place_kernel, dim3(nseg), dim3(kSegThreads), 0, stream, out->topk_ids, T, E, k,
                        cnt, nseg, out->expert_offsets, out->sorted_pairs, out->pair_pos);

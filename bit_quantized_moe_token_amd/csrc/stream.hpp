@@ -117,8 +117,8 @@ __device__ __forceinline__ f16x8 int_bop(const uint32_t *dw, int j, const PairCo
                 int_pair_cz<B>(dw, 4 * j + 2, pc), int_pair_cz<B>(dw, 4 * j + 3, pc));
 }
 
-__device__ __forceinline__ float int_zero(const uint32_t *zz, int q) {
-  return (float)((zz[q >> 2] >> (8 * (q & 3))) & 0xffu);
+__device__ __forceinline__ uint32_t int_zero(const uint32_t *zz, int q) {
+  return (zz[q >> 2] >> (8 * (q & 3))) & 0xffu;
 }
 __device__ __forceinline__ float int_scale(const uint32_t *sc, int q) {
   return (float)__builtin_bit_cast(f16, (uint16_t)(sc[q >> 1] >> (16 * (q & 1))));

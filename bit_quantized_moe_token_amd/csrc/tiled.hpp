@@ -84,7 +84,7 @@ template <int B, int GPT>
 __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
   const int gi = GPT == 2 ? (j >> 1) : 0;
   PairConst pc[9];
-  fill_pair_consts<B>(pc, (float)((tt.zz >> (8 * gi)) & 0xffu));
+  fill_pair_consts<B>(pc, (tt.zz >> (8 * gi)) & 0xffu);
   const f16 s = __builtin_bit_cast(f16, (uint16_t)(tt.sc >> (16 * gi)));
   const f16x2 s2 = {s, s};
   uint32_t p[4];
