@@ -353,11 +353,14 @@ __device__ __forceinline__ void compute_two(const Group<B0, PLANE> &g0, const Gr
 // fragment per MFMA.  The NW waves of the workgroup share the staged
 // activations.  Per group: this group's code loads first, then the next
 // group's activations (publishing those never waits for the codes), then
-// decode + MFMA; the other resident workgroups cover the load latency.
+// decode + MFMA; the other resident workgroups cover the load latency.  The
+// codes of the first group (p0, p1, when it is a full group) are loaded by
+// the caller before its prologue, so they arrive during it.
 template <int NSUB, int NW, int GPT, bool PLANE, int B0, int B1>
 __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc &d1, int s0, int s1,
                                            int g_begin, int g_end, const uint16_t *const *rowp, uint16_t *xs,
-                                           uint16_t *lut_lds, f32x4 (*acc)[NSUB]) {
+                                           uint16_t *lut_lds, f32x4 (*acc)[NSUB], const Group<B0, PLANE> &p0,
+                                           const Group<B1, PLANE> &p1) {
   const int n_kt = d0.K / kTileK;
   const int full = n_kt / 4;                   // groups with 4 tiles
   const int g_full_end = std::min(g_end, full);
@@ -368,20 +371,28 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
     stg.store(xs, lut_lds, c);
     __syncthreads();
   }
-#pragma unroll 1
-  for (int g = g_begin; g < g_full_end; ++g) {
+  // one full group: the next group's activations load, this group is
+  // decoded and multiplied, then the activations are published
+  auto group_step = [&](int g, const Group<B0, PLANE> &c0, const Group<B1, PLANE> &c1) {
     const bool more = g + 1 < g_end;
     const int cn = more ? std::min(4, n_kt - 4 * (g + 1)) : 0;
-    Group<B0, PLANE> c0;
-    Group<B1, PLANE> c1;
-    load_group<B0, PLANE, 4, GPT>(d0, s0, g, n_kt, c0);
-    load_group<B1, PLANE, 4, GPT>(d1, s1, g, n_kt, c1);
     if (more) stg.load(d0, d1, rowp, s0, s1, g + 1, n_kt, cn);
     compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xs, lut_lds, acc);
     if (more) {
       __syncthreads();
       stg.store(xs, lut_lds, cn);
       __syncthreads();
+    }
+  };
+  if (g_begin < g_full_end) {
+    group_step(g_begin, p0, p1);               // codes loaded by the caller up front
+#pragma unroll 1
+    for (int g = g_begin + 1; g < g_full_end; ++g) {
+      Group<B0, PLANE> c0;
+      Group<B1, PLANE> c1;
+      load_group<B0, PLANE, 4, GPT>(d0, s0, g, n_kt, c0);
+      load_group<B1, PLANE, 4, GPT>(d1, s1, g, n_kt, c1);
+      group_step(g, c0, c1);
     }
   }
   if (g_end > full) {                          // the ragged last group
@@ -398,6 +409,17 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
         load_group<B0, PLANE, 3, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 3, GPT>(d1, s1, full, n_kt, t1);
         compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xs, lut_lds, acc); break;
     }
+  }
+}
+
+// Codes of group g of two streams, loaded up front when g is a full group.
+template <int GPT, bool PLANE, int B0, int B1>
+__device__ __forceinline__ void preload_two(const BlockDesc &d0, const BlockDesc &d1, int s0, int s1, int g,
+                                            Group<B0, PLANE> &p0, Group<B1, PLANE> &p1) {
+  const int n_kt = d0.K / kTileK;
+  if (g < n_kt / 4) {
+    load_group<B0, PLANE, 4, GPT>(d0, s0, g, n_kt, p0);
+    load_group<B1, PLANE, 4, GPT>(d1, s1, g, n_kt, p1);
   }
 }
 
@@ -432,20 +454,23 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   uint16_t *xs = lds;
   uint16_t *zs = lds + zs_offset<NSUB>();
   const int zw = 2 * a.RZ;
+  const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];   // scalar loads
+  Group<BG, PLANE> p0;
+  Group<BU, PLANE> p1;
+  preload_two<GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, p0, p1);
   if (a.comp_on) {
     z_prologue<NSUB, 4>(a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, true);
-  const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];   // scalar loads
   f32x4 acc[2][NSUB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.H / kTileK + 3) / 4;
-  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, lut_lds, acc);
+  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, lut_lds, acc, p0, p1);
   const int row = strip * 16 + (lane & 15);
   if (a.comp_on) {
 #pragma unroll
@@ -480,23 +505,25 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   uint16_t *zs = lds + zs_offset<NSUB>();
   const int zw = a.RZ;
   const bool epi = a.comp_on && split == 0;
+  const BlockDesc d = a.desc[3 * ch.e + 2];                          // scalar loads
+  const int n_g4 = (a.I / kTileK + 3) / 4;
+  const int g0 = (int)((int64_t)n_g4 * split / a.splits);
+  const int g1 = (int)((int64_t)n_g4 * (split + 1) / a.splits);
+  const int st0 = 8 * sg + 2 * wave, st1 = st0 + 1;
+  Group<BD, PLANE> p0, p1;
+  if (g1 > g0) preload_two<GPT, PLANE, BD, BD>(d, d, st0, st1, g0, p0, p1);
   if (epi) {
     z_prologue<NSUB, 4>(a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, zw, ch, zs);
     __syncthreads();
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, false);
-  const BlockDesc d = a.desc[3 * ch.e + 2];                          // scalar loads
   f32x4 acc[2][NSUB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n_g4 = (a.I / kTileK + 3) / 4;
-  const int g0 = (int)((int64_t)n_g4 * split / a.splits);
-  const int g1 = (int)((int64_t)n_g4 * (split + 1) / a.splits);
-  const int st0 = 8 * sg + 2 * wave, st1 = st0 + 1;
-  if (g1 > g0) stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, lut_lds, acc);
+  if (g1 > g0) stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, lut_lds, acc, p0, p1);
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
