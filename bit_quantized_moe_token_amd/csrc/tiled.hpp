@@ -9,11 +9,10 @@
 //     registers; down: 256 rows of H);
 //   - 4 waves, each owning 4 strips of 16 rows over all 128 tokens: 32
 //     MFMA 16x16x32 tiles per 32-column step;
-//   - K walks 128-column tiles; the activation tile (128 tokens x 128
-//     columns, rows gathered by token for gate/up) is double-buffered in LDS
-//     with one barrier per tile; each wave loads its strips' packed codes
-//     and scales/zeros for the next tile straight into registers (the
-//     packed layout already is the MFMA B-operand layout);
+//   - K walks 128-column tiles through three LDS stages filled by LDS-DMA
+//     loads two tiles ahead (activation rows gathered by token for gate/up,
+//     XOR-swizzled; the packed codes, whose layout already is the MFMA
+//     B-operand layout per lane), one barrier per tile;
 //   - INT codes decode to fp16 s*(c - z): exact (c - z) from the magic-bias
 //     AND-OR and one packed FMA, then one packed multiply by the group's
 //     fp16 scale (rounded once to fp16);
@@ -25,13 +24,8 @@
 namespace moeq {
 
 constexpr int kTM = kTiledM;           // tokens per token tile
-constexpr int kTS = kTileK + 8;        // LDS row stride (halves) of a staged activation tile
-constexpr int kTBuf = kTM * kTS;       // halves per activation buffer
-constexpr size_t kTiledLdsBytes = (size_t)2 * kTBuf * 2;
-#ifndef MOEQ_TILED_WAVES
-#define MOEQ_TILED_WAVES 8
-#endif
-constexpr int kTiledWaves = MOEQ_TILED_WAVES;   // waves per workgroup: 4 (8 token tiles each) or 8 (4 each)
+constexpr int kTS = kTileK + 8;        // LDS row stride (halves) of the staged h tile
+constexpr int kTiledWaves = 4;   // waves per workgroup (8 token tiles x 4 strips each)
 
 // Packed codes and metadata of one strip for one 128-column tile.
 template <int B>
@@ -56,29 +50,6 @@ __device__ __forceinline__ const uint8_t *tile_word_ptr(const uint8_t *codes, in
   return codes + base + ts + lane * ls;
 }
 
-template <int B, int GPT>
-__device__ __forceinline__ void load_ttile(const BlockDesc &d, int strip, int t, int n_kt, TTile<B> &o) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (B == 4) {
-    const u32x4 v = gld<u32x4>(tile_word_ptr<4>(d.codes, strip, t, 0, n_kt));
-    o.w[0] = v[0]; o.w[1] = v[1]; o.w[2] = v[2]; o.w[3] = v[3];
-  } else if constexpr (B == 2) {
-    const u32x2 v = gld<u32x2>(tile_word_ptr<2>(d.codes, strip, t, 0, n_kt));
-    o.w[0] = v[0]; o.w[1] = v[1];
-  } else {
-#pragma unroll
-    for (int e = 0; e < B; ++e) o.w[e] = gld<uint32_t>(tile_word_ptr<B>(d.codes, strip, t, e, n_kt));
-  }
-  const uint64_t mi = meta_index(strip, t, lane & 15, 0, n_kt, GPT);
-  if constexpr (GPT == 1) {
-    o.sc = gld<uint16_t>(d.scales + mi);
-    o.zz = gld<uint8_t>(d.zeros + mi);
-  } else {
-    o.sc = gld<uint32_t>(d.scales + mi);
-    o.zz = gld<uint16_t>(d.zeros + mi);
-  }
-}
-
 // fp16 B operand s * (c - z) of step j of a tile.
 template <int B, int GPT>
 __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
@@ -93,224 +64,279 @@ __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
   return pack_b(p[0], p[1], p[2], p[3]);
 }
 
-// Activation tile staging by the NW waves of the workgroup: thread tid moves
-// rows (tid / 16) + 4 NW i, 16 B at column 8 (tid % 16), for i < 32 / NW.
-// Row offsets are element offsets from the source base (gathered token rows
-// of x, or contiguous rows of h).
-template <int NW>
-struct TStage {
-  static constexpr int NP = 32 / NW;
-  u32x4 v[NP];
-};
+// ---- LDS stages.  A stage holds one 128-column tile: the activation tile
+// (128 token rows x 256 B, 16-byte slots XOR-swizzled by row so that the
+// MFMA operand reads are bank-conflict free), the packed codes of the
+// workgroup's 16 strips (1 KiB each) and their scales and zeros.  All of
+// it is written by the LDS-DMA form of the global load (global_load_lds):
+// the data never occupies registers, so tiles are fetched two ahead of the
+// MFMAs through three stages, and the only memory counter the loop waits
+// on is the one for these transfers (explicit waits: the compiler does not
+// track DMA writes into LDS).
+constexpr int kTABytes = kTM * 256;
+constexpr int kTBBytes = 16 * 1024;
+constexpr int kTMetaBytes = 4 * 512;                  // per wave: 64 lanes x 2 dword slots
+constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
+constexpr int kTStages = 3;
 
-template <int NW>
-__device__ __forceinline__ void tstage_load(TStage<NW> &st, const uint16_t *src, const uint32_t *rowoff, int kt) {
-  const int col = kt * kTileK + 8 * (threadIdx.x & 15);
-#pragma unroll
-  for (int i = 0; i < TStage<NW>::NP; ++i) st.v[i] = gld<u32x4>(src + rowoff[i] + col);
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(const void *src, uint8_t *lds_base) {
+  const auto g = (const __attribute__((address_space(1))) void *)src;
+  const auto l = (__attribute__((address_space(3))) void *)lds_base;
+  if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+  else if constexpr (SIZE == 4) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+  else if constexpr (SIZE == 2) __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+  else __builtin_amdgcn_global_load_lds(g, l, 1, 0, 0);
 }
 
-template <int NW>
-__device__ __forceinline__ void tstage_store(const TStage<NW> &st, uint16_t *buf) {
-  const int r0 = threadIdx.x >> 4, col = 8 * (threadIdx.x & 15);
-#pragma unroll
-  for (int i = 0; i < TStage<NW>::NP; ++i)
-    *reinterpret_cast<u32x4 *>(buf + (r0 + 4 * NW * i) * kTS + col) = st.v[i];
+// Note on the LDS layout of these transfers: lane l's bytes land at
+// base + l * size for 16- and 4-byte transfers; 1- and 2-byte transfers
+// fill a zero-extended dword slot at base + 4 l.
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ f16x8 tlds_a(const uint16_t *buf, int s, int j) {
+// DMA operations per strip per tile: one 16-byte transfer for 4-bit codes,
+// else one 4-byte transfer per code dword.
+__device__ __forceinline__ constexpr int dma_ops(int B) { return B == 4 ? 1 : B; }
+
+template <int B>
+__device__ __forceinline__ void dma_codes(const BlockDesc &d, int strip, int t, int n_kt, uint8_t *dst) {
+  if constexpr (B == 4) {
+    lds_dma<16>(tile_word_ptr<4>(d.codes, strip, t, 0, n_kt), dst);
+  } else {
+#pragma unroll
+    for (int e = 0; e < B; ++e) lds_dma<4>(tile_word_ptr<B>(d.codes, strip, t, e, n_kt), dst + 256 * e);
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void lds_codes(const uint8_t *src, TTile<B> &tt) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const f16x8 *>(buf + (16 * s + (lane & 15)) * kTS + 32 * j + 8 * (lane >> 4));
+  if constexpr (B == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * lane);
+    tt.w[0] = v[0]; tt.w[1] = v[1]; tt.w[2] = v[2]; tt.w[3] = v[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < B; ++e) tt.w[e] = *reinterpret_cast<const uint32_t *>(src + 256 * e + 4 * lane);
+  }
 }
 
-// The four strips of a wave: q = 0, 1 from block d0 (bits B0), q = 2, 3
-// from block d1 (bits B1).
-template <int B0, int B1>
-struct TSet {
-  TTile<B0> a0, a1;
-  TTile<B1> b0, b1;
-};
+// Operand A of token tile s, step j from the swizzled activation tile.
+__device__ __forceinline__ f16x8 tlds_a(const uint8_t *abuf, int s, int j) {
+  const int lane = threadIdx.x & 63;
+  const int row = 16 * s + (lane & 15), c = 4 * j + (lane >> 4);
+  return *reinterpret_cast<const f16x8 *>(abuf + row * 256 + 16 * (c ^ (row & 15)));
+}
 
+// The strips of wave w: q = 0, 1 from block d0 (bits B0), q = 2, 3 from d1
+// (bits B1); their codes sit at 1 KiB slots 4 w + q of the stage, their
+// scales/zeros in lanes 16 q .. 16 q + 15 of the wave's metadata slots.
 template <int B0, int B1, int GPT>
-__device__ __forceinline__ void tset_load(TSet<B0, B1> &ts, const BlockDesc &d0, const BlockDesc &d1,
-                                          const int *strips, int t, int n_kt) {
-  load_ttile<B0, GPT>(d0, strips[0], t, n_kt, ts.a0);
-  load_ttile<B0, GPT>(d0, strips[1], t, n_kt, ts.a1);
-  load_ttile<B1, GPT>(d1, strips[2], t, n_kt, ts.b0);
-  load_ttile<B1, GPT>(d1, strips[3], t, n_kt, ts.b1);
-}
+struct TKLoop {
+  static constexpr int kDma = 8 + 2 * dma_ops(B0) + 2 * dma_ops(B1) + 2;   // DMA ops per tile per wave
+  const BlockDesc &d0, &d1;
+  const int *strips;
+  int n_kt, wave;
+  const uint16_t *src;
+  const uint32_t *rowoff;
+  uint8_t *lds;
 
-// One 128-column tile: NT token tiles (starting at token tile t0) x 4 strips.
-template <int B0, int B1, int GPT, int NT>
-__device__ __forceinline__ void tset_compute(const TSet<B0, B1> &ts, const uint16_t *buf, int t0,
-                                             f32x4 (*acc)[NT]) {
+  __device__ __forceinline__ uint8_t *stage(int st) const { return lds + st * kTStageBytes; }
+
+  // tile t into stage st: the wave's 8 KiB share of the activation tile,
+  // its strips' codes, scales and zeros
+  __device__ __forceinline__ void issue(int t, int st) const {
+    const int lane = threadIdx.x & 63;
+    uint8_t *a = stage(st);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x8 w0 = tdecode<B0, GPT>(ts.a0, j), w1 = tdecode<B0, GPT>(ts.a1, j);
-    const f16x8 w2 = tdecode<B1, GPT>(ts.b0, j), w3 = tdecode<B1, GPT>(ts.b1, j);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 32 * wave + 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      lds_dma<16>(src + rowoff[i] + t * kTileK + 8 * c, a + (32 * wave + 4 * i) * 256);
+    }
+    uint8_t *b = stage(st) + kTABytes + 4 * wave * 1024;
+    dma_codes<B0>(d0, strips[0], t, n_kt, b);
+    dma_codes<B0>(d0, strips[1], t, n_kt, b + 1024);
+    dma_codes<B1>(d1, strips[2], t, n_kt, b + 2048);
+    dma_codes<B1>(d1, strips[3], t, n_kt, b + 3072);
+    // lane l: strip q = l / 16, row l % 16
+    const int q = lane >> 4;
+    const BlockDesc &dq = q < 2 ? d0 : d1;
+    const uint64_t mi = meta_index(strips[q], t, lane & 15, 0, n_kt, GPT);
+    uint8_t *m = stage(st) + kTABytes + kTBBytes + wave * 512;
+    lds_dma<2 * GPT>(dq.scales + mi, m);       // dword slot per lane
+    lds_dma<GPT>(dq.zeros + mi, m + 256);      // zero-extended dword slot per lane
+  }
+
+  template <int NT>
+  __device__ __forceinline__ void compute(int st, f32x4 (*acc)[NT]) const {
+    const int lane = threadIdx.x & 63;
+    const uint8_t *a = stage(st);
+    const uint8_t *b = stage(st) + kTABytes + 4 * wave * 1024;
+    const uint8_t *m = stage(st) + kTABytes + kTBBytes + wave * 512;
+    TTile<B0> t0, t1;
+    TTile<B1> t2, t3;
+    lds_codes<B0>(b, t0);
+    lds_codes<B0>(b + 1024, t1);
+    lds_codes<B1>(b + 2048, t2);
+    lds_codes<B1>(b + 3072, t3);
+    const int r = lane & 15;
+    const uint32_t *sc = reinterpret_cast<const uint32_t *>(m);
+    const uint32_t *zz = reinterpret_cast<const uint32_t *>(m + 256);
+    t0.sc = sc[r]; t1.sc = sc[16 + r]; t2.sc = sc[32 + r]; t3.sc = sc[48 + r];
+    t0.zz = zz[r]; t1.zz = zz[16 + r]; t2.zz = zz[32 + r]; t3.zz = zz[48 + r];
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      const f16x8 av = tlds_a(buf, t0 + s, j);
-      acc[0][s] = mfma16(av, w0, acc[0][s]);
-      acc[1][s] = mfma16(av, w1, acc[1][s]);
-      acc[2][s] = mfma16(av, w2, acc[2][s]);
-      acc[3][s] = mfma16(av, w3, acc[3][s]);
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 w0 = tdecode<B0, GPT>(t0, j), w1 = tdecode<B0, GPT>(t1, j);
+      const f16x8 w2 = tdecode<B1, GPT>(t2, j), w3 = tdecode<B1, GPT>(t3, j);
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        const f16x8 av = tlds_a(a, s, j);
+        acc[0][s] = mfma16(av, w0, acc[0][s]);
+        acc[1][s] = mfma16(av, w1, acc[1][s]);
+        acc[2][s] = mfma16(av, w2, acc[2][s]);
+        acc[3][s] = mfma16(av, w3, acc[3][s]);
+      }
     }
   }
-}
 
-// The K loop over all n_kt tiles, unrolled by two so that the register
-// sets and LDS buffers of consecutive tiles alternate without copies.  The
-// body has no branches: the prefetch after the last tile re-reads the last
-// tile (its data is never used).
-template <int B0, int B1, int GPT, int NW, int NT>
-__device__ __forceinline__ void tiled_kloop(const BlockDesc &d0, const BlockDesc &d1, const int *strips, int n_kt,
-                                            const uint16_t *src, const uint32_t *rowoff, uint16_t *lds, int t0,
-                                            f32x4 (*acc)[NT]) {
-  uint16_t *buf0 = lds, *buf1 = lds + kTBuf;
-  TSet<B0, B1> s0, s1;
-  TStage<NW> st;
-  tstage_load<NW>(st, src, rowoff, 0);
-  tset_load<B0, B1, GPT>(s0, d0, d1, strips, 0, n_kt);
-  tstage_store<NW>(st, buf0);
-  __syncthreads();
-  int kt = 0;
+  // one K tile: wait for its stage (the next tile's transfers may stay in
+  // flight), barrier (every wave's transfers done; every wave has finished
+  // reading the stage of tile t - 1), queue tile t + 2 into that stage,
+  // multiply
+  template <int ST, int NT>
+  __device__ __forceinline__ void step(int t, f32x4 (*acc)[NT]) const {
+    vm_wait<kDma>();
+    __builtin_amdgcn_s_barrier();
+    issue(std::min(t + 2, n_kt - 1), (ST + 2) % 3);
+    compute<NT>(ST, acc);
+  }
+
+  template <int NT>
+  __device__ __forceinline__ void run(f32x4 (*acc)[NT]) const {
+    issue(0, 0);
+    issue(std::min(1, n_kt - 1), 1);
+    int kt = 0;
 #pragma unroll 1
-  for (; kt + 2 <= n_kt; kt += 2) {
-    tstage_load<NW>(st, src, rowoff, kt + 1);
-    tset_load<B0, B1, GPT>(s1, d0, d1, strips, kt + 1, n_kt);
-    tset_compute<B0, B1, GPT, NT>(s0, buf0, t0, acc);
-    tstage_store<NW>(st, buf1);
-    __syncthreads();
-    const int kn = std::min(kt + 2, n_kt - 1);
-    tstage_load<NW>(st, src, rowoff, kn);
-    tset_load<B0, B1, GPT>(s0, d0, d1, strips, kn, n_kt);
-    tset_compute<B0, B1, GPT, NT>(s1, buf1, t0, acc);
-    tstage_store<NW>(st, buf0);
+    for (; kt + 3 <= n_kt; kt += 3) {
+      step<0, NT>(kt, acc);
+      step<1, NT>(kt + 1, acc);
+      step<2, NT>(kt + 2, acc);
+    }
+    if (kt < n_kt) step<0, NT>(kt, acc);
+    if (kt + 1 < n_kt) step<1, NT>(kt + 1, acc);
+    // the queued re-reads of the last tile land before the LDS is reused
+    vm_wait<0>();
     __syncthreads();
   }
-  if (kt < n_kt) {            // odd tile count: the last tile is in set 0 / buffer 0
-    tset_compute<B0, B1, GPT, NT>(s0, buf0, t0, acc);
-    __syncthreads();
-  }
-}
+};
 
 // Workgroup b of n (n a multiple of 8): workgroups are dealt to the 8 XCDs
 // round-robin, so logical tile L = (b % 8) * (n / 8) + b / 8 gives each
 // XCD a contiguous run of tiles.
 __device__ __forceinline__ int xcd_tile(int b, int n) { return (b & 7) * (n >> 3) + (b >> 3); }
 
-// Wave w of NW: strip group wn = w % 4, token tiles NT * (w / 4) + [0, NT)
-// with NT = 32 / NW.
-template <int NW>
-struct TWave {
-  static constexpr int NT = 32 / NW;
-  int wn, t0;
-  __device__ __forceinline__ TWave() {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wn = w & 3;
-    t0 = NT * (w >> 2);
+// gate/up: wave w owns I rows nt*128 + 32 w + [0, 32) of gate (q = 0, 1)
+// and up (q = 2, 3), for all 128 tokens of the tile.
+template <int BG, int BU, int GPT>
+__device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];
+  const int sg = nt * 8 + 2 * wave;
+  const int strips[4] = {sg, sg + 1, sg, sg + 1};
+  uint32_t rowoff[8];          // activation rows this lane moves: 32 w + 4 i + lane / 16
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
+    rowoff[i] = (uint32_t)(a.sorted_pairs[ch.base + m] / a.k) * (uint32_t)a.H;
   }
-};
-
-template <int NW>
-__device__ __forceinline__ void zero_acc(f32x4 (*acc)[32 / NW]) {
+  f32x4 acc[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int s = 0; s < 32 / NW; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// gate/up: strip group wn owns I rows nt*128 + 32 wn + [0, 32) of gate
-// (q = 0, 1) and up (q = 2, 3).
-template <int BG, int BU, int GPT, int NW>
-__device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk &ch, int nt, uint16_t *lds) {
-  constexpr int NT = 32 / NW, NP = 32 / NW;
-  const int lane = threadIdx.x & 63, tid = threadIdx.x;
-  const TWave<NW> w;
-  const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];
-  const int sg = nt * 8 + 2 * w.wn;
-  const int strips[4] = {sg, sg + 1, sg, sg + 1};
-  uint32_t rowoff[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int m = std::min((tid >> 4) + 4 * NW * i, ch.cnt - 1);
-    rowoff[i] = (uint32_t)(a.sorted_pairs[ch.base + m] / a.k) * (uint32_t)a.H;
-  }
-  f32x4 acc[4][NT];
-  zero_acc<NW>(acc);
-  tiled_kloop<BG, BU, GPT, NW, NT>(dg, du, strips, a.H / kTileK, a.x, rowoff, lds, w.t0, acc);
-  // the loop ends with a barrier: the activation buffers are free
+    for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const TKLoop<BG, BU, GPT> kl{dg, du, strips, a.H / kTileK, wave, a.x, rowoff, lds};
+  kl.template run<8>(acc);
+  uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
-    uint16_t *zs = lds;
+    uint16_t *zs = l16;
     const int zw = 2 * a.RZ;
-    z_prologue<8, NW>(a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    z_prologue<8, 4>(a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
-    const uint16_t *zw0 = zs + 16 * w.t0 * zw;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int b = q >> 1;
       const BlockDesc &d = b ? du : dg;
       const int row = strips[q] * 16 + (lane & 15);
-      if (a.r > 0) lowrank_epi<NT>(d.U, a.r, a.Rp, row, zw0 + b * a.RZ, zw, acc[q]);
-      if (a.rs > 0) lowrank_epi<NT>(d.Us, a.rs, a.Rsp, row, zw0 + b * a.RZ + a.Rp, zw, acc[q]);
+      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[q]);
+      if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[q]);
     }
     __syncthreads();
   }
   // h = SiLU(gate) * up into LDS [128 tokens][128 columns], then coalesced rows
-  uint16_t *hs = lds;
+  uint16_t *hs = l16;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int col = 32 * w.wn + 16 * g + (lane & 15);
+    const int col = 32 * wave + 16 * g + (lane & 15);
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float gv = acc[g][s][i], uv = acc[2 + g][s][i];
         const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        hs[(16 * (w.t0 + s) + 4 * (lane >> 4) + i) * kTS + col] = __builtin_bit_cast(uint16_t, (f16)hv);
+        hs[(16 * s + 4 * (lane >> 4) + i) * kTS + col] = __builtin_bit_cast(uint16_t, (f16)hv);
       }
     }
   }
   __syncthreads();
-  const int c8 = 8 * (tid & 15);
+  const int tid = threadIdx.x, c8 = 8 * (tid & 15);
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int r = (tid >> 4) + 4 * NW * i;
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 4) + 16 * i;
     if (r < ch.cnt)
       *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + r) * a.I + nt * kTileK + c8) =
           *reinterpret_cast<const u32x4 *>(hs + r * kTS + c8);
   }
 }
 
-// down: strip group wn owns H rows nt*256 + 64 wn + [0, 64).
-template <int BD, int GPT, int NW>
-__device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &ch, int nt, uint16_t *lds) {
-  constexpr int NT = 32 / NW, NP = 32 / NW;
-  const int lane = threadIdx.x & 63, tid = threadIdx.x;
-  const TWave<NW> w;
+// down: wave w owns H rows nt*256 + 64 w + [0, 64).
+template <int BD, int GPT>
+__device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BlockDesc d = a.desc[3 * ch.e + 2];
-  const int s0 = nt * 16 + 4 * w.wn;
+  const int s0 = nt * 16 + 4 * wave;
   const int strips[4] = {s0, s0 + 1, s0 + 2, s0 + 3};
-  uint32_t rowoff[NP];
+  uint32_t rowoff[8];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int m = std::min((tid >> 4) + 4 * NW * i, ch.cnt - 1);
+  for (int i = 0; i < 8; ++i) {
+    const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
     rowoff[i] = (uint32_t)(ch.base + m) * (uint32_t)a.I;
   }
-  f32x4 acc[4][NT];
-  zero_acc<NW>(acc);
-  tiled_kloop<BD, BD, GPT, NW, NT>(d, d, strips, a.I / kTileK, a.h, rowoff, lds, w.t0, acc);
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const TKLoop<BD, BD, GPT> kl{d, d, strips, a.I / kTileK, wave, a.h, rowoff, lds};
+  kl.template run<8>(acc);
   if (a.comp_on) {
-    uint16_t *zs = lds;
-    z_prologue<8, NW>(a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
+    uint16_t *zs = reinterpret_cast<uint16_t *>(lds);
+    z_prologue<8, 4>(a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
     __syncthreads();
-    const uint16_t *zw0 = zs + 16 * w.t0 * a.RZ;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = strips[q] * 16 + (lane & 15);
-      if (a.r > 0) lowrank_epi<NT>(d.U, a.r, a.Rp, row, zw0, a.RZ, acc[q]);
-      if (a.rs > 0) lowrank_epi<NT>(d.Us, a.rs, a.Rsp, row, zw0 + a.Rp, a.RZ, acc[q]);
+      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs, a.RZ, acc[q]);
+      if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + a.Rp, a.RZ, acc[q]);
     }
   }
   float *yp = a.ypart;
@@ -318,10 +344,10 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   for (int q = 0; q < 4; ++q) {
     const int row = strips[q] * 16 + (lane & 15);
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 16 * (w.t0 + s) + 4 * (lane >> 4) + i;
+        const int m = 16 * s + 4 * (lane >> 4) + i;
         if (m < ch.cnt) yp[(int64_t)(ch.base + m) * a.H + row] = acc[q][s][i];
       }
     }
@@ -329,9 +355,9 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
 }
 
 // grid.x = (upper bound of token tiles) * (I / 128), rounded up to 8
-template <int GPT, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) tiled_gateup_kernel(FfnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t tl_lds[];
+template <int GPT>
+__global__ void __launch_bounds__(256, 1) tiled_gateup_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.I / kTileK;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = L / n_nt, nt = L % n_nt;
@@ -339,32 +365,34 @@ __global__ void __launch_bounds__(64 * NW, 1) tiled_gateup_kernel(FfnArgs a) {
   if (!find_chunk<kTM>(a.offsets, a.E, mt, &ch)) return;
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
-    case 2 * 4 + 2: tiled_gateup_body<2, 2, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 2 * 4 + 3: tiled_gateup_body<2, 3, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 2 * 4 + 4: tiled_gateup_body<2, 4, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 2: tiled_gateup_body<3, 2, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 3: tiled_gateup_body<3, 3, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 4: tiled_gateup_body<3, 4, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 4 * 4 + 2: tiled_gateup_body<4, 2, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 4 * 4 + 3: tiled_gateup_body<4, 3, GPT, NW>(a, ch, nt, tl_lds); break;
-    default: tiled_gateup_body<4, 4, GPT, NW>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 2: tiled_gateup_body<2, 2, GPT>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 3: tiled_gateup_body<2, 3, GPT>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 4: tiled_gateup_body<2, 4, GPT>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 2: tiled_gateup_body<3, 2, GPT>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 3: tiled_gateup_body<3, 3, GPT>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 4: tiled_gateup_body<3, 4, GPT>(a, ch, nt, tl_lds); break;
+    case 4 * 4 + 2: tiled_gateup_body<4, 2, GPT>(a, ch, nt, tl_lds); break;
+    case 4 * 4 + 3: tiled_gateup_body<4, 3, GPT>(a, ch, nt, tl_lds); break;
+    default: tiled_gateup_body<4, 4, GPT>(a, ch, nt, tl_lds); break;
   }
 }
 
 // grid.x = (upper bound of token tiles) * (H / 256), rounded up to 8
-template <int GPT, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) tiled_down_kernel(FfnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t tl_lds[];
+template <int GPT>
+__global__ void __launch_bounds__(256, 1) tiled_down_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.H / 256;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = L / n_nt, nt = L % n_nt;
   Chunk ch;
   if (!find_chunk<kTM>(a.offsets, a.E, mt, &ch)) return;
   switch (a.desc[3 * ch.e + 2].bits) {
-    case 2: tiled_down_body<2, GPT, NW>(a, ch, nt, tl_lds); break;
-    case 3: tiled_down_body<3, GPT, NW>(a, ch, nt, tl_lds); break;
-    default: tiled_down_body<4, GPT, NW>(a, ch, nt, tl_lds); break;
+    case 2: tiled_down_body<2, GPT>(a, ch, nt, tl_lds); break;
+    case 3: tiled_down_body<3, GPT>(a, ch, nt, tl_lds); break;
+    default: tiled_down_body<4, GPT>(a, ch, nt, tl_lds); break;
   }
 }
+
+constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
 
 }  // namespace moeq

@@ -5,9 +5,9 @@ namespace moeq {
 
 void launch_tiled_gateup(const FfnArgs &a, int grid, hipStream_t s) {
   if (a.G == 64)
-    hipLaunchKernelGGL((tiled_gateup_kernel<2, kTiledWaves>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
+    hipLaunchKernelGGL((tiled_gateup_kernel<2>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
   else
-    hipLaunchKernelGGL((tiled_gateup_kernel<1, kTiledWaves>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
+    hipLaunchKernelGGL((tiled_gateup_kernel<1>), dim3(grid), dim3(64 * kTiledWaves), kTiledLdsBytes, s, a);
 }
 
 }  // namespace moeq
