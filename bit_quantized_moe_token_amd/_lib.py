@@ -58,6 +58,8 @@ SIGNATURES = [
     ("moeq_debug_unpack", c_i32, [c_void_p, c_i32, c_i32, c_void_p, c_void_p]),
     ("moeq_route_workspace_size", c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_route", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing), c_void_p, c_size_t, c_void_p]),
+    ("moeq_route_mass", c_i32, [ctypes.POINTER(Routing), c_i32, c_i32, c_i32, c_void_p, c_i32, c_void_p,
+                                c_void_p, c_void_p]),
     ("moeq_ffn_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions), ctypes.POINTER(c_size_t)]),
     ("moeq_expert_ffn", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
                                 c_void_p, c_i32, c_void_p, c_size_t, ctypes.POINTER(FfnOptions), c_void_p]),

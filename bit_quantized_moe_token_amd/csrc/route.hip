@@ -270,6 +270,39 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, const i
 
 static inline int route_segments(int T) { return (T + kSegTokens - 1) / kSegTokens; }
 
+// Routing mass (PagedWeight review summary: routing-mass buckets protect
+// frequently used experts): m_e = sum of the gates of expert e's pairs.
+// One wave per expert: lane-strided partial sums over the expert's sorted
+// pairs, then a fixed xor-shuffle tree, so the result is deterministic.
+// bucket_e = number of edges <= m_e.
+constexpr int kMaxEdges = 8;
+struct MassEdges {
+  float v[kMaxEdges];
+  int n;
+};
+
+__global__ void __launch_bounds__(256)
+route_mass_kernel(const float *__restrict__ gates, const int32_t *__restrict__ offsets,
+                  const int32_t *__restrict__ sorted_pairs, int E, MassEdges ed, float *__restrict__ mass,
+                  int32_t *__restrict__ bucket) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int lo = offsets[e], hi = offsets[e + 1];
+  float acc = 0.f;
+  for (int pos = lo + lane; pos < hi; pos += kWave) acc += gates[sorted_pairs[pos]];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (lane == 0) {
+    mass[e] = acc;
+    if (bucket) {
+      int b = 0;
+      for (int i = 0; i < ed.n; ++i) b += ed.v[i] <= acc ? 1 : 0;
+      bucket[e] = b;
+    }
+  }
+}
+
 }  // namespace moeq
 
 using namespace moeq;
@@ -317,4 +350,27 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
   }
   prof_end("route", stream);
   return check_launch("route");
+}
+
+MOEQ_API moeq_status moeq_route_mass(const moeq_routing *r, int32_t T, int32_t E, int32_t k, const float *edges,
+                                     int32_t n_edges, float *mass, int32_t *bucket, hipStream_t stream) {
+  if (!r) return fail(MOEQ_ERR_INVALID, "route_mass: null routing");
+  if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E)
+    return fail(MOEQ_ERR_INVALID, "route_mass: T=%d E=%d k=%d invalid", T, E, k);
+  if (n_edges < 0 || n_edges > kMaxEdges || (n_edges > 0 && !edges))
+    return fail(MOEQ_ERR_INVALID, "route_mass: n_edges=%d not in 0..%d (or null edges)", n_edges, kMaxEdges);
+  MassEdges ed{};
+  ed.n = n_edges;
+  for (int i = 0; i < n_edges; ++i) {
+    if (!(edges[i] == edges[i]) || (i > 0 && edges[i] < edges[i - 1]))
+      return fail(MOEQ_ERR_INVALID, "route_mass: edges must be ascending and not NaN");
+    ed.v[i] = edges[i];
+  }
+  if (!mass || !r->expert_offsets || (T > 0 && (!r->topk_gates || !r->sorted_pairs)))
+    return fail(MOEQ_ERR_INVALID, "route_mass: null pointer");
+  prof_begin("route_mass", stream);
+  hipLaunchKernelGGL(route_mass_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, r->topk_gates, r->expert_offsets,
+                     r->sorted_pairs, E, ed, mass, bucket);
+  prof_end("route_mass", stream);
+  return check_launch("route_mass");
 }

@@ -6,6 +6,7 @@ the library filled.  No arithmetic of the method happens here.
 """
 
 import ctypes
+from ctypes import c_void_p
 
 import numpy as np
 import torch
@@ -192,6 +193,18 @@ def route(logits, k, out=None):
     check(lib().moeq_route(_ptr(logits), T, E, k, ctypes.byref(out.c), _ptr(out.ws), out.ws_bytes, _stream()),
           "moeq_route")
     return out
+
+
+def route_mass(routing, edges=()):
+    """Per-expert routing mass and (with edges) bucket index (see moeq_route_mass)."""
+    E = routing.E
+    mass = torch.empty((E,), dtype=torch.float32, device=routing.ids.device)
+    bucket = torch.empty((E,), dtype=torch.int32, device=routing.ids.device) if len(edges) else None
+    ed = (ctypes.c_float * max(1, len(edges)))(*[float(v) for v in edges])
+    check(lib().moeq_route_mass(ctypes.byref(routing.c), routing.T, E, routing.k,
+                                ctypes.cast(ed, c_void_p) if len(edges) else None, len(edges),
+                                _ptr(mass), _ptr(bucket), _stream()), "moeq_route_mass")
+    return mass, bucket
 
 
 # ------------------------------------------------------------ expert FFN

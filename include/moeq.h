@@ -221,6 +221,22 @@ moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32_t k,
                        const moeq_routing *out, void *ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/*
+ * moeq_route_mass — gate-weighted routing mass of every expert from a
+ * routing of T tokens: mass[e] = sum of topk_gates over the pairs routed
+ * to e ([PW] review summary: the planner's routing-mass buckets protect
+ * frequently used experts; the mass is the per-expert usage they bucket),
+ * and optionally bucket[e] = number of edges <= mass[e].  fp32, summed in
+ * a fixed order (deterministic); the masses of all experts add up to T
+ * within rounding.
+ *   r      routing of T tokens, top-k, E experts (from moeq_route).
+ *   edges  HOST [n_edges] ascending bucket edges, n_edges in 0..8 (NULL if 0).
+ *   mass   DEVICE [E] fp32 output.  bucket DEVICE [E] int32 output or NULL.
+ */
+moeq_status moeq_route_mass(const moeq_routing *r, int32_t T, int32_t E, int32_t k,
+                            const float *edges, int32_t n_edges, float *mass, int32_t *bucket,
+                            hipStream_t stream);
+
 /* ---------------------------------------------------------- expert FFN -- */
 
 typedef enum {

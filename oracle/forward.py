@@ -90,6 +90,25 @@ def route(logits, k):
                 sorted_pairs=sorted_pairs, pair_pos=pair_pos)
 
 
+def routing_mass(ids, gates, E):
+    """Gate-weighted routing mass of each expert: m_e = sum over (t, j) with
+    ids[t, j] == e of gates[t, j] (float64), the per-expert usage measure
+    that PagedWeight's planner buckets ("Routing-mass buckets", review
+    summary; the planner's routing-bucket multiplier)."""
+    m = np.zeros(E, dtype=np.float64)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            m[int(ids[t, j])] += float(gates[t, j])
+    return m
+
+
+def mass_bucket(mass, edges):
+    """Bucket index of each mass against ascending edges: the number of
+    edges that are <= the mass (bucket b holds edges[b-1] <= m < edges[b])."""
+    edges = np.asarray(edges, dtype=np.float64)
+    return np.array([int(np.sum(edges <= m)) for m in np.asarray(mass)], dtype=np.int32)
+
+
 # ----------------------------------------------------------------- dequant
 
 def dequant_int(codes, s16, z, G):

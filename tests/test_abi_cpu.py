@@ -72,6 +72,17 @@ def test_route_validation(L):
                         None) == 3
 
 
+def test_route_mass_validation_cpu(L):
+    from bit_quantized_moe_token_amd import _lib
+    r = _lib.Routing(16, 16, 16, 16, 16)
+    edges = (ctypes.c_float * 2)(2.0, 1.0)
+    assert L.moeq_route_mass(ctypes.byref(r), 4, 8, 2, ctypes.cast(edges, ctypes.c_void_p), 2,
+                             ctypes.c_void_p(16), None, None) == 1        # descending edges
+    assert L.moeq_route_mass(ctypes.byref(r), 4, 8, 2, None, 9, ctypes.c_void_p(16), None, None) == 1
+    assert L.moeq_route_mass(ctypes.byref(r), 4, 8, 9, None, 0, ctypes.c_void_p(16), None, None) == 1
+    assert L.moeq_route_mass(ctypes.byref(r), 4, 8, 2, None, 0, None, None, None) == 1   # null mass
+
+
 def _desc(E=2, H=256, I=512, G=64, fmt=0, bits=4, r=0):
     from bit_quantized_moe_token_amd import _lib
     nb = 3 * E

@@ -59,3 +59,41 @@ def test_route_deterministic():
     b = _route(logits, 2)
     for f in ("ids", "gates", "offsets", "sorted_pairs", "pair_pos"):
         assert torch.equal(getattr(a, f), getattr(b, f))
+
+
+# ---- routing mass (per-expert gate-weighted usage and its buckets)
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "finegrained", "bitplane"])
+def test_route_mass(name):
+    from bit_quantized_moe_token_amd import moeq
+    cfg = configs.get(name)
+    logits = gen.gen_logits(cfg, 0)
+    rt = _route(logits, cfg["k"])
+    ref = forward.route(logits, cfg["k"])
+    m_ref = forward.routing_mass(ref["ids"], ref["gates"], cfg["E"])
+    # edges around the typical mass, including one at an exactly representable value
+    mean = cfg["T"] * cfg["k"] / cfg["E"] / cfg["k"]
+    edges = [0.0, 0.5 * mean, mean, 2.0 * mean, 4.0]
+    edges = sorted(edges)
+    mass, bucket = moeq.route_mass(rt, edges)
+    torch.cuda.synchronize()
+    m = mass.cpu().numpy().astype(np.float64)
+    # fp32 sums of at most T gates in [0, 1]
+    assert np.all(np.abs(m - m_ref) <= 1e-5 * np.maximum(1.0, m_ref)), np.max(np.abs(m - m_ref))
+    assert abs(m.sum() - cfg["T"]) <= 1e-5 * cfg["T"]
+    # the bucket decision is taken on the kernel's fp32 mass
+    b_host = forward.mass_bucket(mass.cpu().numpy(), np.asarray(edges, dtype=np.float32))
+    assert np.array_equal(bucket.cpu().numpy(), b_host)
+    far = np.min(np.abs(m_ref[:, None] - np.asarray(edges)[None, :]), axis=1) > 1e-3
+    assert np.array_equal(bucket.cpu().numpy()[far], forward.mass_bucket(m_ref, edges)[far])
+    mass2, _ = moeq.route_mass(rt)
+    assert torch.equal(mass, mass2)                     # deterministic; no buckets requested
+
+
+def test_route_mass_validation():
+    from bit_quantized_moe_token_amd import moeq
+    rt = _route(np.zeros((4, 8), dtype=np.float32), 2)
+    with pytest.raises(moeq.MoeqError):
+        moeq.route_mass(rt, [2.0, 1.0])                  # not ascending
+    with pytest.raises(moeq.MoeqError):
+        moeq.route_mass(rt, list(range(9)))              # too many edges

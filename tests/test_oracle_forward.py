@@ -73,6 +73,34 @@ def test_counting_sort_matches_stable_argsort(E, P):
         assert np.all(np.diff(ids[sp]) >= 0)
 
 
+def test_routing_mass_pins():
+    """Routing mass: brute-force per-expert sums of the gates; k = E gives
+    the full softmax column sums; the masses of all experts add up to T
+    (every token's gates sum to 1); bucket edges by counting."""
+    rng = np.random.default_rng(11)
+    T, E = 37, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    for k in (1, 2, E):
+        rt = forward.route(logits, k)
+        m = forward.routing_mass(rt["ids"], rt["gates"], E)
+        brute = np.array([sum(rt["gates"][t, j] for t in range(T) for j in range(k) if rt["ids"][t, j] == e)
+                          for e in range(E)])
+        assert np.allclose(m, brute, rtol=0, atol=1e-12)
+        assert abs(m.sum() - T) < 1e-12
+        if k == E:
+            l = logits.astype(np.float64)
+            p = np.exp(l - l.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            assert np.allclose(m, p.sum(0), rtol=0, atol=1e-12)
+    # k = 1 mass is the count of tokens whose top expert is e
+    rt = forward.route(logits, 1)
+    assert np.array_equal(forward.routing_mass(rt["ids"], rt["gates"], E),
+                          np.bincount(rt["ids"][:, 0], minlength=E).astype(np.float64))
+    edges = [1.0, 4.0, 9.5]
+    assert forward.mass_bucket([0.0, 0.99, 1.0, 3.9, 4.0, 9.5, 100.0], edges).tolist() == [0, 0, 1, 1, 2, 3, 3]
+    assert forward.mass_bucket([5.0], []).tolist() == [0]
+
+
 # ------------------------------------------------------------------ toy layers
 
 class _DictLayer:
