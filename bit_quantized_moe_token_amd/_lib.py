@@ -56,6 +56,10 @@ SIGNATURES = [
     ("moeq_layer_block_bytes", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_layer_shared_bytes", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_debug_unpack", c_i32, [c_void_p, c_i32, c_i32, c_void_p, c_void_p]),
+    ("moeq_commit_bits", c_i32, [c_void_p, c_i32, c_i32, c_i32, c_void_p, c_void_p]),
+    ("moeq_committed_bits", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_i32)]),
+    ("moeq_plane_region", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(c_void_p),
+                                  ctypes.POINTER(c_size_t)]),
     ("moeq_route_workspace_size", c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_route", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing), c_void_p, c_size_t, c_void_p]),
     ("moeq_route_mass", c_i32, [ctypes.POINTER(Routing), c_i32, c_i32, c_i32, c_void_p, c_i32, c_void_p,

@@ -247,7 +247,9 @@ static Plan make_plan(const moeq_layer_desc *d) {
     } else {
       off = align256(off + 4 * align256(nk / 8));
       p.lut_off[b] = off;
-      off = align256(off + (nk / kTileK) * ((size_t)2 << bits));
+      // room for a 16-entry table per (row, tile): a later commit to any q
+      // rewrites the table in place
+      off = align256(off + (nk / kTileK) * 32);
     }
     if (d->r > 0) {
       p.U_off[b] = off; off = align256(off + (size_t)N * d->r * 2);
@@ -421,4 +423,57 @@ MOEQ_API moeq_status moeq_debug_unpack(const moeq_layer *L, int32_t e, int32_t b
   }
   prof_end("debug_unpack", stream);
   return check_launch("debug_unpack");
+}
+
+namespace moeq {
+
+// Stream-ordered update of one block's committed bit-plane count.
+__global__ void set_bits_kernel(BlockDesc *d, int32_t bits) { d->bits = bits; }
+
+}  // namespace moeq
+
+MOEQ_API moeq_status moeq_commit_bits(moeq_layer *L, int32_t e, int32_t blk, int32_t q, const uint16_t *lut,
+                                      hipStream_t stream) {
+  if (!L) return fail(MOEQ_ERR_INVALID, "commit_bits: null layer");
+  if (e < 0 || e >= L->dims.E || blk < 0 || blk > 2) return fail(MOEQ_ERR_INVALID, "commit_bits: bad block (%d,%d)", e, blk);
+  if (L->dims.fmt != MOEQ_FMT_BITPLANE)
+    return fail(MOEQ_ERR_UNSUPPORTED, "commit_bits: only bit-plane layers change bitwidth after packing");
+  if (q < 2 || q > 4) return fail(MOEQ_ERR_INVALID, "commit_bits: q=%d not in {2,3,4}", q);
+  if (!lut) return fail(MOEQ_ERR_INVALID, "commit_bits: null LUT");
+  const int b = 3 * e + blk;
+  BlockDesc &bd = L->h_desc[b];
+  const int n_kt = bd.K / kTileK;
+  prof_begin("commit_bits", stream);
+  hipLaunchKernelGGL(pack_lut_kernel, dim3(nblocks((int64_t)bd.N * n_kt << q)), dim3(256), 0, stream,
+                     lut, bd.N, bd.K, q, const_cast<uint16_t *>(bd.lut));
+  hipLaunchKernelGGL(set_bits_kernel, dim3(1), dim3(1), 0, stream, L->d_desc + b, q);
+  prof_end("commit_bits", stream);
+  moeq_status st = check_launch("commit_bits");
+  if (st != MOEQ_OK) return st;
+  const size_t nk = (size_t)bd.N * bd.K;
+  const size_t old_codes = nk * bd.bits / 8 + (nk / kTileK) * ((size_t)2 << bd.bits);
+  const size_t new_codes = nk * q / 8 + (nk / kTileK) * ((size_t)2 << q);
+  L->block_alg_bytes[b] = L->block_alg_bytes[b] - old_codes + new_codes;
+  bd.bits = q;
+  L->bits[b] = (uint8_t)q;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_committed_bits(const moeq_layer *L, int32_t e, int32_t blk, int32_t *q) {
+  if (!L || !q) return fail(MOEQ_ERR_INVALID, "committed_bits: null argument");
+  if (e < 0 || e >= L->dims.E || blk < 0 || blk > 2) return fail(MOEQ_ERR_INVALID, "committed_bits: bad block (%d,%d)", e, blk);
+  *q = L->h_desc[3 * e + blk].bits;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_plane_region(const moeq_layer *L, int32_t e, int32_t blk, int32_t plane, void **ptr,
+                                       size_t *bytes) {
+  if (!L || !ptr || !bytes) return fail(MOEQ_ERR_INVALID, "plane_region: null argument");
+  if (e < 0 || e >= L->dims.E || blk < 0 || blk > 2) return fail(MOEQ_ERR_INVALID, "plane_region: bad block (%d,%d)", e, blk);
+  if (L->dims.fmt != MOEQ_FMT_BITPLANE) return fail(MOEQ_ERR_UNSUPPORTED, "plane_region: not a bit-plane layer");
+  if (plane < 0 || plane > 3) return fail(MOEQ_ERR_INVALID, "plane_region: plane=%d not in 0..3", plane);
+  const BlockDesc &bd = L->h_desc[3 * e + blk];
+  *ptr = const_cast<uint8_t *>(bd.codes) + (size_t)plane * bd.plane_bytes;
+  *bytes = bd.plane_bytes;
+  return MOEQ_OK;
 }

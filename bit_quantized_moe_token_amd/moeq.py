@@ -154,6 +154,25 @@ class PackedLayer:
         check(lib().moeq_debug_unpack(self.handle, e, blk, _ptr(out), _stream()), "moeq_debug_unpack")
         return out
 
+    def commit_bits(self, e, blk, q, lut):
+        """Commit bit-plane count q of block (e, blk) with its LUT [N, K/G, 16]
+        (see moeq_commit_bits); stream-ordered on the current stream."""
+        N, K = self.block_shape(blk)
+        _need(lut, torch.float16, (N, K // self.G, 16), "lut")
+        check(lib().moeq_commit_bits(self.handle, e, blk, q, _ptr(lut), _stream()), "moeq_commit_bits")
+
+    def committed_bits(self, e, blk):
+        q = ctypes.c_int32(0)
+        check(lib().moeq_committed_bits(self.handle, e, blk, ctypes.byref(q)), "moeq_committed_bits")
+        return q.value
+
+    def plane_region(self, e, blk, plane):
+        """(device address, bytes) of bit-plane `plane` (0 = most significant)."""
+        ptr, n = c_void_p(0), ctypes.c_size_t(0)
+        check(lib().moeq_plane_region(self.handle, e, blk, plane, ctypes.byref(ptr), ctypes.byref(n)),
+              "moeq_plane_region")
+        return ptr.value, n.value
+
 
 def quantize_block(w, fmt, bits, G):
     """Quantize one fp16 block with the library's kernels into the pack input

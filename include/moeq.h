@@ -190,6 +190,36 @@ moeq_status moeq_layer_shared_bytes(const moeq_layer *L, int32_t group, int32_t 
 moeq_status moeq_debug_unpack(const moeq_layer *L, int32_t e, int32_t blk,
                               uint8_t *out, hipStream_t stream);
 
+/*
+ * Runtime bitwidth of bit-plane blocks ([PW] "What carries the argument":
+ * each expert linear block is a weight page of bit-planes plus the lookup
+ * table of its committed bitwidth q; a page's bitwidth is lowered or
+ * restored at run time and a change takes effect only once committed).
+ *
+ * moeq_commit_bits — make q the committed bit-plane count of block (e, blk)
+ * for every call enqueued on `stream` after this one: the block's table is
+ * rewritten from `lut` and its descriptor updated, both on `stream` (calls
+ * already enqueued read the previous state; callers using several streams
+ * order them themselves).  From then on the kernels read planes 0 .. q-1
+ * (plane 0 = most significant) and the q-bit table.
+ *   lut DEVICE [N][K/G][16] fp16, slots [0, 2^q) used (as from
+ *   moeq_build_lut with this q); read during the call's stream work.
+ *   Bit-plane layers only (MOEQ_ERR_UNSUPPORTED for INT); q in {2,3,4}.
+ *   moeq_layer_block_bytes reports the new committed bytes afterwards.
+ *
+ * moeq_committed_bits — the committed q of a block (host-side state).
+ *
+ * moeq_plane_region — where plane `plane` (0 = most significant) of a
+ * bit-plane block lives inside the packed buffer, and its size, so that a
+ * caller can page a plane out (copy to host, reuse the bytes) while no
+ * committed q reads it, and copy it back before committing a q that does.
+ */
+moeq_status moeq_commit_bits(moeq_layer *L, int32_t expert, int32_t block, int32_t q,
+                             const uint16_t *lut, hipStream_t stream);
+moeq_status moeq_committed_bits(const moeq_layer *L, int32_t expert, int32_t block, int32_t *q);
+moeq_status moeq_plane_region(const moeq_layer *L, int32_t expert, int32_t block, int32_t plane,
+                              void **ptr, size_t *bytes);
+
 /* ------------------------------------------------------------- routing -- */
 
 /* Routing outputs, all DEVICE, caller-owned; P = T * k. */

@@ -15,9 +15,10 @@ FRO_REL = 2e-3
 GATE_ATOL = 2e-6
 
 
-def oracle_layer(cfg, seed, cache_blocks=8):
+def oracle_layer(cfg, seed, cache_blocks=8, bits=None):
+    """bits: per-block b / q [E, 3] (default: the generator's draw)."""
     E, H, I, G = cfg["E"], cfg["H"], cfg["I"], cfg["G"]
-    bits = gen.gen_bits(cfg, seed)
+    bits = gen.gen_bits(cfg, seed) if bits is None else np.asarray(bits, dtype=np.uint8)
     svd = cfg.get("comp") == "svd"
 
     def rows(e, blk, r):

@@ -83,6 +83,15 @@ def test_route_mass_validation_cpu(L):
     assert L.moeq_route_mass(ctypes.byref(r), 4, 8, 2, None, 0, None, None, None) == 1   # null mass
 
 
+def test_commit_validation_cpu(L):
+    # null layer / output pointers are rejected before any device work
+    q = ctypes.c_int32(0)
+    assert L.moeq_commit_bits(None, 0, 0, 3, ctypes.c_void_p(16), None) == 1
+    assert L.moeq_committed_bits(None, 0, 0, ctypes.byref(q)) == 1
+    p, n = ctypes.c_void_p(0), ctypes.c_size_t(0)
+    assert L.moeq_plane_region(None, 0, 0, 0, ctypes.byref(p), ctypes.byref(n)) == 1
+
+
 def _desc(E=2, H=256, I=512, G=64, fmt=0, bits=4, r=0):
     from bit_quantized_moe_token_amd import _lib
     nb = 3 * E
