@@ -62,6 +62,11 @@ SIGNATURES = [
                                   ctypes.POINTER(c_size_t)]),
     ("moeq_route_workspace_size", c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_route", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing), c_void_p, c_size_t, c_void_p]),
+    ("moeq_plan_reductions", c_i32, [c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.c_double, ctypes.c_double,
+                                     ctypes.POINTER(c_i32), c_i32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32)]),
     ("moeq_route_mass", c_i32, [ctypes.POINTER(Routing), c_i32, c_i32, c_i32, c_void_p, c_i32, c_void_p,
                                 c_void_p, c_void_p]),
     ("moeq_ffn_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions), ctypes.POINTER(c_size_t)]),

@@ -226,6 +226,27 @@ def route_mass(routing, edges=()):
     return mass, bucket
 
 
+def plan_reductions(q, bytes_tbl, g, mu, eta, eps, target):
+    """Greedy bit-plane release plan (see moeq_plan_reductions); host arrays.
+    Returns (planned q, block of each action in order, released bytes, damage)."""
+    q = np.ascontiguousarray(q, dtype=np.int32).copy()
+    n = q.shape[0]
+    bt = np.ascontiguousarray(bytes_tbl, dtype=np.float64).reshape(n, 3)
+    gg = np.ascontiguousarray(g, dtype=np.float64).reshape(n, 3)
+    mu = np.ascontiguousarray(mu, dtype=np.float64).reshape(n)
+    eta = np.ascontiguousarray(eta, dtype=np.float64).reshape(n)
+    cap = int(2 * n) + 1
+    order = np.zeros(cap, dtype=np.int32)
+    rel, dmg, na = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int32(0)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    check(lib().moeq_plan_reductions(n, q.ctypes.data_as(ip), bt.ctypes.data_as(dp), gg.ctypes.data_as(dp),
+                                     mu.ctypes.data_as(dp), eta.ctypes.data_as(dp), float(eps), float(target),
+                                     order.ctypes.data_as(ip), cap, ctypes.byref(rel), ctypes.byref(dmg),
+                                     ctypes.byref(na)), "moeq_plan_reductions")
+    return q, order[:na.value].tolist(), rel.value, dmg.value
+
+
 # ------------------------------------------------------------ expert FFN
 
 class FfnWorkspace:

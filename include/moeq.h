@@ -220,6 +220,27 @@ moeq_status moeq_committed_bits(const moeq_layer *L, int32_t expert, int32_t blo
 moeq_status moeq_plane_region(const moeq_layer *L, int32_t expert, int32_t block, int32_t plane,
                               void **ptr, size_t *bytes);
 
+/*
+ * moeq_plan_reductions — host-side planner of bit-plane releases ([PW]
+ * "What carries the argument": the planner turns a byte target into page
+ * releases, taking actions in order of predicted damage per released byte,
+ * damage = max(eps, mu_i * g_i * eta_i)).  An action lowers block i's
+ * committed bit-plane count by one; while the released bytes are below
+ * `target` the available action with the least damage per released byte is
+ * taken (ties: lower block index); target <= 0 takes none; q stops at 2.
+ *   n blocks; q HOST [n] committed counts in 2..4, overwritten with the plan;
+ *   bytes HOST [n][3] page bytes of each block at q = 2, 3, 4 (increasing);
+ *   g HOST [n][3] sensitivity of each block at q = 2, 3, 4 (the damage of
+ *   an action uses g at the bitwidth it lowers to); mu, eta HOST [n];
+ *   eps >= 0; order HOST [max_actions] receives the block of each action
+ *   (may be NULL when max_actions is 0); released, damage, n_actions HOST.
+ * Pure host code: no device work, no stream.
+ */
+moeq_status moeq_plan_reductions(int32_t n, int32_t *q, const double *bytes, const double *g,
+                                 const double *mu, const double *eta, double eps, double target,
+                                 int32_t *order, int32_t max_actions, double *released,
+                                 double *damage, int32_t *n_actions);
+
 /* ------------------------------------------------------------- routing -- */
 
 /* Routing outputs, all DEVICE, caller-owned; P = T * k. */
