@@ -76,6 +76,9 @@ __device__ __forceinline__ T gld_nt(const void *p) {
 // takes no literal operand, so with literal m and c the compiler would emit
 // a v_and_b32 and a v_or_b32; the asm operands make it keep the constants
 // in registers (hoisted out of loops) and issue the single instruction.
+// Its result must not be an MFMA operand without a compiler-emitted
+// instruction in between: the compiler does not count inline asm when it
+// inserts the wait states between a VALU write and an MFMA read.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
@@ -84,6 +87,37 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Global -> LDS transfer of SIZE bytes per lane (global_load_lds): the
+// compiler does not track these LDS writes, so callers wait with vm_wait
+// before reading the data and order LDS reuse themselves.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(const void *src, uint8_t *lds_base) {
+  const auto g = (const __attribute__((address_space(1))) void *)src;
+  const auto l = (__attribute__((address_space(3))) void *)lds_base;
+  if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+  else if constexpr (SIZE == 4) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+  else if constexpr (SIZE == 2) __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+  else __builtin_amdgcn_global_load_lds(g, l, 1, 0, 0);
+}
+
+// Note on the LDS layout of these transfers: lane l's bytes land at
+// base + l * size for 16- and 4-byte transfers; 1- and 2-byte transfers
+// fill a zero-extended dword slot at base + 4 l.
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ f16x8 pack_b(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(f16x8, v);
+}
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -76,11 +76,6 @@ __device__ __forceinline__ f16x8 load_a(const uint16_t *p) {
   return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
-__device__ __forceinline__ f16x8 pack_b(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  u32x4 v = {a, b, c, d};
-  return __builtin_bit_cast(f16x8, v);
-}
-
 // Upper bound of the number of chunks of MT pairs for T tokens, top-k, E
 // experts (an expert holds at most T pairs).
 inline int max_chunks(int E, int T, int k, int MT = kMT) {

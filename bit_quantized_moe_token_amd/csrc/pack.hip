@@ -30,28 +30,18 @@ pack_int_kernel(const uint8_t *__restrict__ codes, int N, int K, uint8_t *__rest
   const int s = (int)((id >> 6) / n_kt);
   const int row = s * kStripRows + (l & 15);
   const uint8_t *src = codes + (int64_t)row * K;
-  uint32_t d[B];
-#pragma unroll
-  for (int e = 0; e < B; ++e) d[e] = 0;
+  uint32_t d[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int P = 0; P < 16; ++P) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t c = src[tile_col(t, l, P, h)] & ((1u << B) - 1);
-      if (B == 4) {
-        const int j = P >> 2, v = P & 3;
-        d[j] |= c << (16 * h + 4 * v);
-      } else if (B == 3) {
-        if (P == 15) {
+      const Field f = int_field<B>(P);
+      if (f.e < 0) {
 #pragma unroll
-          for (int e = 0; e < 3; ++e) d[e] |= ((c >> e) & 1u) << (15 + 16 * h);
-        } else {
-          const int e = P / 5, u = P % 5;
-          d[e] |= c << (16 * h + 3 * u);
-        }
+        for (int i = 0; i < 3; ++i) d[i] |= ((c >> i) & 1u) << (16 * h + spare3_bit(i));
       } else {
-        const int e = P >> 3, u = P & 7;
-        d[e] |= c << (16 * h + 2 * u);
+        d[f.e] |= c << (16 * h + f.s + f.p);
       }
     }
   }

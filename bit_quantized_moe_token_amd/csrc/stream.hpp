@@ -43,20 +43,8 @@ struct Group {
 };
 
 template <int B, int C, int GPT>
-__device__ __forceinline__ void load_int_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, false> &g) {
-  const int lane = threadIdx.x & 63, r = lane & 15;
-  const uint8_t *p = d.codes + int_word_offset(strip, 4 * g4, lane, 0, n_kt, B);
-  if (C == 4) {
-    // chunk i of the group: 1 KiB of consecutive bytes across the wave
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const u32x4 v = gld_nt<u32x4>(p + 1024 * i);
-      g.w[4 * i] = v[0]; g.w[4 * i + 1] = v[1]; g.w[4 * i + 2] = v[2]; g.w[4 * i + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < C * B; ++i) g.w[i] = gld<uint32_t>(p + 4 * i);
-  }
+__device__ __forceinline__ void load_int_meta(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, false> &g) {
+  const int r = threadIdx.x & 15;
   const uint64_t mi = meta_index(strip, 4 * g4, r, 0, n_kt, GPT);
   const uint16_t *sp = d.scales + mi;
   const uint8_t *zp = d.zeros + mi;
@@ -78,6 +66,24 @@ __device__ __forceinline__ void load_int_group(const BlockDesc &d, int strip, in
       g.zz[q >> 2] |= (uint32_t)gld<uint8_t>(zp + q) << (8 * (q & 3));
     }
   }
+}
+
+template <int B, int C, int GPT>
+__device__ __forceinline__ void load_int_group(const BlockDesc &d, int strip, int g4, int n_kt, Group<B, false> &g) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t *p = d.codes + int_word_offset(strip, 4 * g4, lane, 0, n_kt, B);
+  if (C == 4) {
+    // chunk i of the group: 1 KiB of consecutive bytes across the wave
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const u32x4 v = gld_nt<u32x4>(p + 1024 * i);
+      g.w[4 * i] = v[0]; g.w[4 * i + 1] = v[1]; g.w[4 * i + 2] = v[2]; g.w[4 * i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C * B; ++i) g.w[i] = gld<uint32_t>(p + 4 * i);
+  }
+  load_int_meta<B, C, GPT>(d, strip, g4, n_kt, g);
 }
 
 template <int Q, int C>
@@ -110,13 +116,6 @@ __device__ __forceinline__ f16x8 lds_a(const uint16_t *xs, int s, int tl, int j)
                                           32 * j + 8 * (lane >> 4));
 }
 
-// Decoded B operand of step j of tile tl (INT: exact (c - z) pairs).
-template <int B>
-__device__ __forceinline__ f16x8 int_bop(const uint32_t *dw, int j, const PairConst *pc) {
-  return pack_b(int_pair_cz<B>(dw, 4 * j + 0, pc), int_pair_cz<B>(dw, 4 * j + 1, pc),
-                int_pair_cz<B>(dw, 4 * j + 2, pc), int_pair_cz<B>(dw, 4 * j + 3, pc));
-}
-
 __device__ __forceinline__ uint32_t int_zero(const uint32_t *zz, int q) {
   return (zz[q >> 2] >> (8 * (q & 3))) & 0xffu;
 }
@@ -126,44 +125,52 @@ __device__ __forceinline__ float int_scale(const uint32_t *sc, int q) {
 
 // One group of C tiles for NB INT blocks sharing the A operands: each
 // activation fragment read from LDS feeds the MFMAs of every block before
-// the next is read.  Per quantization group: fp32 partial sums of
-// (c - z) * x, then acc += scale * partial.
+// the next is read.  The staged activations are pre-scaled for b0's field
+// pattern (block 1 re-scales a fragment to its own pattern when its
+// bitwidth differs), so the subnormal-form B operands give, per
+// quantization group and token subtile, P_b = 2^-24 sum c x.  With
+// S = -2^-24 sum x of the group's columns (per token, staged in LDS next to
+// the activations), acc_b += s_b (P_b + z_b S) = 2^-24 s_b sum (c - z) x.
+// The accumulators stay in units of 2^-24 until the end of the K walk.
 template <int NSUB, int NB, int B0, int B1, int C, int GPT>
 __device__ __forceinline__ void compute_int(const Group<B0, false> &g0, const Group<B1, false> &g1,
-                                            const uint16_t *xs, f32x4 (*acc)[NSUB]) {
+                                            const uint16_t *xs, const float *sx, f32x4 (*acc)[NSUB]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int tl = 0; tl < C; ++tl) {
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
       const int q = tl * GPT + gi;
-      PairConst pc0[9], pc1[9];
-      fill_pair_consts<B0>(pc0, int_zero(g0.zz, q));
-      if (NB == 2) fill_pair_consts<B1>(pc1, int_zero(g1.zz, q));
       f32x4 p0[NSUB], p1[NSUB];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) { p0[s] = f32x4{0.f, 0.f, 0.f, 0.f}; p1[s] = p0[s]; }
 #pragma unroll
       for (int jj = 0; jj < 4 / GPT; ++jj) {
         const int j = gi * (4 / GPT) + jj;
-        const f16x8 b0 = int_bop<B0>(g0.w + tl * B0, j, pc0);
+        const f16x8 b0 = int_bop_sub<B0>(g0.w + tl * B0, j);
         f16x8 b1;
-        if (NB == 2) b1 = int_bop<B1>(g1.w + tl * B1, j, pc1);
+        if (NB == 2) b1 = int_bop_sub<B1>(g1.w + tl * B1, j);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
           const f16x8 av = lds_a(xs, s, tl, j);
           p0[s] = mfma16(av, b0, p0[s]);
-          if (NB == 2) p1[s] = mfma16(av, b1, p1[s]);
+          if (NB == 2) p1[s] = mfma16(rescale_a<B0, B1>(av), b1, p1[s]);
         }
       }
-      const float s0 = int_scale(g0.sc, q);
+      const float z0 = (float)int_zero(g0.zz, q), s0 = int_scale(g0.sc, q);
+      const float z1 = NB == 2 ? (float)int_zero(g1.zz, q) : 0.f;
       const float s1 = NB == 2 ? int_scale(g1.sc, q) : 0.f;
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
+        const f32x4 sv = *reinterpret_cast<const f32x4 *>(sx + q * (NSUB * 16) + 16 * s + 4 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[0][s][i] = __builtin_fmaf(s0, p0[s][i], acc[0][s][i]);
-          if (NB == 2) acc[1][s][i] = __builtin_fmaf(s1, p1[s][i], acc[1][s][i]);
+          acc[0][s][i] = __builtin_fmaf(s0, __builtin_fmaf(z0, sv[i], p0[s][i]), acc[0][s][i]);
+          if (NB == 2) acc[1][s][i] = __builtin_fmaf(s1, __builtin_fmaf(z1, sv[i], p1[s][i]), acc[1][s][i]);
         }
+        // keep the group's update here (not sunk past later groups), so its
+        // partial sums die at once
+        asm volatile("" : "+v"(acc[0][s]), "+v"(acc[1][s]));
       }
     }
   }
@@ -234,13 +241,48 @@ __device__ __forceinline__ void stage_load(XStage<NSUB, NW> &st, const uint16_t 
   for (int p = 0; p < XStage<NSUB, NW>::NP; ++p) st.v[p] = gld<u32x4>(rowp[p] + col);
 }
 
-template <int NSUB, int NW>
-__device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t *xs, int c) {
+// One DPP lane permutation of a float (ctrl: a DPP control constant).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum of a float over the lanes of each DPP row (16 lanes) or half-row (8).
+template <int LANES>
+__device__ __forceinline__ float row_sum(float t) {
+  t += dpp_f<0xb1>(t);                         // quad_perm [1,0,3,2]
+  t += dpp_f<0x4e>(t);                         // quad_perm [2,3,0,1]
+  t += dpp_f<0x141>(t);                        // row_half_mirror
+  if constexpr (LANES == 16) t += dpp_f<0x140>(t);   // row_mirror
+  return t;
+}
+
+// PS > 0 (INT codes of PS bits): besides storing the row, write
+// S = -2^-24 * (sum of the row's columns) per quantization group (GPT per
+// tile) to sx[(tile * GPT + group) * NSUB*16 + row], then pre-scale the
+// columns for the field pattern (dword v of a lane's 16 bytes holds the two
+// columns of register v).  Lane l holds columns 8l..8l+7 of the 4-tile row,
+// so the 16 lanes of a DPP row are one tile.
+template <int NSUB, int NW, int PS, int GPT>
+__device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t *xs, float *sx, int c) {
   (void)c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int p = 0; p < XStage<NSUB, NW>::NP; ++p)
-    *reinterpret_cast<u32x4 *>(xs + (NW * p + wave) * kXStride + 8 * lane) = st.v[p];
+  for (int p = 0; p < XStage<NSUB, NW>::NP; ++p) {
+    const int row = NW * p + wave;
+    u32x4 v = st.v[p];
+    if constexpr (PS > 0) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t = __builtin_amdgcn_fdot2(as_h2(v[w]), f16x2{1.0f16, 1.0f16}, t, false);
+      constexpr int L = 16 / GPT;
+      t = row_sum<L>(t);
+      if ((lane & (L - 1)) == 0) sx[(lane / L) * (NSUB * 16) + row] = t * -0x1p-24f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[w] = prescale_pair<PS>(v[w], w);
+    }
+    *reinterpret_cast<u32x4 *>(xs + row * kXStride + 8 * lane) = v;
+  }
 }
 
 // LUT staging of one wave's strip for a group: 4 tiles x 16 rows x NQ
@@ -319,7 +361,7 @@ __device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, 
 
 // Stage group g's activations (and the two streams' bit-plane LUTs) into
 // LDS: load, then (after the caller's barrier) store.
-template <int NSUB, int NW, bool PLANE, int B0, int B1>
+template <int NSUB, int NW, bool PLANE, int B0, int B1, int GPT>
 struct Stager {
   XStage<NSUB, NW> st;
   LutStage<B0> l0;
@@ -332,8 +374,8 @@ struct Stager {
       lut_load<B1>(d1, s1, g4, n_kt, c, l1);
     }
   }
-  __device__ __forceinline__ void store(uint16_t *xs, uint16_t *lut_lds, int c) {
-    stage_store<NSUB, NW>(st, xs, c);
+  __device__ __forceinline__ void store(uint16_t *xs, float *sx, uint16_t *lut_lds, int c) {
+    stage_store<NSUB, NW, PLANE ? 0 : B0, GPT>(st, xs, sx, c);
     if constexpr (PLANE) {
       lut_store<B0>(l0, lut_lds, c);
       lut_store<B1>(l1, lut_lds + kLutBlk, c);
@@ -343,32 +385,34 @@ struct Stager {
 
 template <int NSUB, int B0, int B1, bool PLANE, int C, int GPT>
 __device__ __forceinline__ void compute_two(const Group<B0, PLANE> &g0, const Group<B1, PLANE> &g1,
-                                            const uint16_t *xs, const uint16_t *lut, f32x4 (*acc)[NSUB]) {
+                                            const uint16_t *xs, const float *sx, const uint16_t *lut,
+                                            f32x4 (*acc)[NSUB]) {
   if constexpr (PLANE) compute_plane<NSUB, 2, B0, B1, C>(g0, g1, xs, lut, acc);
-  else compute_int<NSUB, 2, B0, B1, C, GPT>(g0, g1, xs, acc);
+  else compute_int<NSUB, 2, B0, B1, C, GPT>(g0, g1, xs, sx, acc);
 }
 
 // Streams tile groups [g_begin, g_end) of two weight streams per wave —
 // (block d0, strip s0) and (block d1, strip s1) — that share one activation
 // fragment per MFMA.  The NW waves of the workgroup share the staged
-// activations.  Per group: this group's code loads first, then the next
-// group's activations (publishing those never waits for the codes), then
-// decode + MFMA; the other resident workgroups cover the load latency.  The
-// codes of the first group (p0, p1, when it is a full group) are loaded by
-// the caller before its prologue, so they arrive during it.
+// activations (and, for INT codes, the per-group column sums in sx).  Per
+// group: this group's code loads first, then the next group's activations
+// (publishing those never waits for the codes), then decode + MFMA; the
+// other resident workgroups cover the load latency.  The codes of the
+// first group (m0, m1, when it is a full group) are loaded by the caller
+// before its prologue, so they arrive during it.
 template <int NSUB, int NW, int GPT, bool PLANE, int B0, int B1>
 __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc &d1, int s0, int s1,
                                            int g_begin, int g_end, const uint16_t *const *rowp, uint16_t *xs,
-                                           uint16_t *lut_lds, f32x4 (*acc)[NSUB], const Group<B0, PLANE> &p0,
-                                           const Group<B1, PLANE> &p1) {
+                                           float *sx, uint16_t *lut_lds, f32x4 (*acc)[NSUB],
+                                           const Group<B0, PLANE> &m0, const Group<B1, PLANE> &m1) {
   const int n_kt = d0.K / kTileK;
   const int full = n_kt / 4;                   // groups with 4 tiles
   const int g_full_end = std::min(g_end, full);
-  Stager<NSUB, NW, PLANE, B0, B1> stg;
+  Stager<NSUB, NW, PLANE, B0, B1, GPT> stg;
   {
     const int c = std::min(4, n_kt - 4 * g_begin);
     stg.load(d0, d1, rowp, s0, s1, g_begin, n_kt, c);
-    stg.store(xs, lut_lds, c);
+    stg.store(xs, sx, lut_lds, c);
     __syncthreads();
   }
   // one full group: the next group's activations load, this group is
@@ -377,15 +421,15 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
     const bool more = g + 1 < g_end;
     const int cn = more ? std::min(4, n_kt - 4 * (g + 1)) : 0;
     if (more) stg.load(d0, d1, rowp, s0, s1, g + 1, n_kt, cn);
-    compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xs, lut_lds, acc);
+    compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xs, sx, lut_lds, acc);
     if (more) {
       __syncthreads();
-      stg.store(xs, lut_lds, cn);
+      stg.store(xs, sx, lut_lds, cn);
       __syncthreads();
     }
   };
   if (g_begin < g_full_end) {
-    group_step(g_begin, p0, p1);               // codes loaded by the caller up front
+    group_step(g_begin, m0, m1);               // codes loaded by the caller up front
 #pragma unroll 1
     for (int g = g_begin + 1; g < g_full_end; ++g) {
       Group<B0, PLANE> c0;
@@ -401,14 +445,20 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
     switch (n_kt - 4 * full) {
       case 1:
         load_group<B0, PLANE, 1, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 1, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 1, GPT>(t0, t1, xs, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 1, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
       case 2:
         load_group<B0, PLANE, 2, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 2, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 2, GPT>(t0, t1, xs, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 2, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
       default:
         load_group<B0, PLANE, 3, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 3, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xs, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
     }
+  }
+  if constexpr (!PLANE) {                      // INT sums are in units of 2^-24
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[b][s] *= 16777216.0f;
   }
 }
 
@@ -441,16 +491,28 @@ __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a
   }
 }
 
-// LDS layout of both stream kernels: [x staging | z rows | LUTs].
+// LDS layout of both stream kernels: [x staging | z rows (2 RZ columns) |
+// per-group column sums (4 tiles x 2 groups x NSUB*16 rows, fp32) | per wave:
+// its two streams' bit-plane LUTs].
 template <int NSUB>
 __device__ __forceinline__ int zs_offset() { return NSUB * 16 * kXStride; }
+
+template <int NSUB>
+__device__ __forceinline__ float *sx_region(uint16_t *lds, int RZ) {
+  return reinterpret_cast<float *>(lds + NSUB * 16 * kXStride + NSUB * 16 * 2 * RZ);
+}
+
+template <int NSUB>
+__device__ __forceinline__ uint16_t *lut_region(uint16_t *lds, int RZ, int wave) {
+  return reinterpret_cast<uint16_t *>(sx_region<NSUB>(lds, RZ) + 8 * NSUB * 16) + wave * 2 * kLutBlk;
+}
 
 // gate/up: 4 waves, each streams the gate and the up rows of one 16-row
 // strip; h = SiLU(gate) * up is formed in registers.
 template <int NSUB, int GPT, bool PLANE, int BG, int BU>
-__device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *lds,
-                                            uint16_t *lut_lds) {
+__device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *lds) {
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t *xs = lds;
   uint16_t *zs = lds + zs_offset<NSUB>();
   const int zw = 2 * a.RZ;
@@ -470,7 +532,8 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.H / kTileK + 3) / 4;
-  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, lut_lds, acc, p0, p1);
+  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, sx_region<NSUB>(lds, a.RZ),
+                                          lut_region<NSUB>(lds, a.RZ, wave), acc, p0, p1);
   const int row = strip * 16 + (lane & 15);
   if (a.comp_on) {
 #pragma unroll
@@ -497,8 +560,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
 // down: 4 waves, each streams two 16-row strips of the down block over the
 // split's K range.
 template <int NSUB, int GPT, bool PLANE, int BD>
-__device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int sg, int split, uint16_t *lds,
-                                          uint16_t *lut_lds) {
+__device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int sg, int split, uint16_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t *xs = lds;
@@ -523,7 +585,9 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (g1 > g0) stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, lut_lds, acc, p0, p1);
+  if (g1 > g0)
+    stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, sx_region<NSUB>(lds, a.RZ),
+                                            lut_region<NSUB>(lds, a.RZ, wave), acc, p0, p1);
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -553,22 +617,15 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
 // exits at once.
 __device__ __forceinline__ int nsub_of(int cnt) { return cnt <= 16 ? 1 : (cnt <= 32 ? 2 : 4); }
 
-// LDS bytes of one class: x staging, z rows (up to 2 blocks x 128 columns),
-// per-wave LUTs (bit-plane: 2 streams per wave).
-inline size_t stream_lds_bytes(bool plane, int nsub) {
-  size_t b = (size_t)nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 256 * 2;
-  if (plane) b += (size_t)4 * 2 * kLutBlk * 2;
-  return b;
-}
-
-template <int NSUB>
-__device__ __forceinline__ uint16_t *lut_region(uint16_t *lds, int wave) {
-  return lds + NSUB * 16 * kXStride + NSUB * 16 * 256 + wave * 2 * kLutBlk;
+// LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
+inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
+  return (size_t)nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 2 * RZ * 2 + (size_t)8 * nsub * 16 * 4 +
+         (plane ? (size_t)4 * 2 * kLutBlk * 2 : 0);
 }
 
 // gate/up: 256 threads; grid.x = max_chunks * (I / 64)
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 2 : 1)) gateup_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) gateup_kernel(FfnArgs a) {
   uint16_t *lds = dyn_lds();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_sg = a.I / 64;
@@ -576,57 +633,54 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 2 : 1)) gate
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
   const int strip = 4 * sg + wave;
-  uint16_t *ll = lut_region<NSUB>(lds, wave);
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
-    case 2 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 2, 2>(a, ch, strip, lds, ll); break;
-    case 2 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 2, 3>(a, ch, strip, lds, ll); break;
-    case 2 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 2, 4>(a, ch, strip, lds, ll); break;
-    case 3 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 3, 2>(a, ch, strip, lds, ll); break;
-    case 3 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 3, 3>(a, ch, strip, lds, ll); break;
-    case 3 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 3, 4>(a, ch, strip, lds, ll); break;
-    case 4 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 4, 2>(a, ch, strip, lds, ll); break;
-    case 4 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 4, 3>(a, ch, strip, lds, ll); break;
-    default: gateup_body<NSUB, GPT, PLANE, 4, 4>(a, ch, strip, lds, ll); break;
+    case 2 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 2, 2>(a, ch, strip, lds); break;
+    case 2 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 2, 3>(a, ch, strip, lds); break;
+    case 2 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 2, 4>(a, ch, strip, lds); break;
+    case 3 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 3, 2>(a, ch, strip, lds); break;
+    case 3 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 3, 3>(a, ch, strip, lds); break;
+    case 3 * 4 + 4: gateup_body<NSUB, GPT, PLANE, 3, 4>(a, ch, strip, lds); break;
+    case 4 * 4 + 2: gateup_body<NSUB, GPT, PLANE, 4, 2>(a, ch, strip, lds); break;
+    case 4 * 4 + 3: gateup_body<NSUB, GPT, PLANE, 4, 3>(a, ch, strip, lds); break;
+    default: gateup_body<NSUB, GPT, PLANE, 4, 4>(a, ch, strip, lds); break;
   }
 }
 
 // down: 256 threads, 128 rows; grid.x = max_chunks * (H / 128) * splits
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 2 : 1)) down_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) down_kernel(FfnArgs a) {
   uint16_t *lds = dyn_lds();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_sg = a.H / 128;
   const int split = blockIdx.x % a.splits;
   const int rest = blockIdx.x / a.splits;
   const int chunk = rest / n_sg, sg = rest % n_sg;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
-  uint16_t *ll = lut_region<NSUB>(lds, wave);
   switch (a.desc[3 * ch.e + 2].bits) {
-    case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, sg, split, lds, ll); break;
-    case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, sg, split, lds, ll); break;
-    default: down_body<NSUB, GPT, PLANE, 4>(a, ch, sg, split, lds, ll); break;
+    case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, sg, split, lds); break;
+    case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, sg, split, lds); break;
+    default: down_body<NSUB, GPT, PLANE, 4>(a, ch, sg, split, lds); break;
   }
 }
 
 // Launch helpers for one (GPT, PLANE) class, instantiated in the .hip files.
 template <int GPT, bool PLANE>
 void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1), s, a);
+  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
   if (a.nsub_max >= 2)
-    hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2), s, a);
+    hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
   if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4), s, a);
+    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
 }
 
 template <int GPT, bool PLANE>
 void launch_down_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1), s, a);
+  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
   if (a.nsub_max >= 2)
-    hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2), s, a);
+    hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
   if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4), s, a);
+    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
 }
 
 void launch_gateup_g128(const FfnArgs &a, int grid, hipStream_t s);

@@ -79,29 +79,6 @@ constexpr int kTMetaBytes = 4 * 512;                  // per wave: 64 lanes x 2 
 constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
 constexpr int kTStages = 3;
 
-template <int SIZE>
-__device__ __forceinline__ void lds_dma(const void *src, uint8_t *lds_base) {
-  const auto g = (const __attribute__((address_space(1))) void *)src;
-  const auto l = (__attribute__((address_space(3))) void *)lds_base;
-  if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-  else if constexpr (SIZE == 4) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-  else if constexpr (SIZE == 2) __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
-  else __builtin_amdgcn_global_load_lds(g, l, 1, 0, 0);
-}
-
-// Note on the LDS layout of these transfers: lane l's bytes land at
-// base + l * size for 16- and 4-byte transfers; 1- and 2-byte transfers
-// fill a zero-extended dword slot at base + 4 l.
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at
-// their maxima).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // DMA operations per strip per tile: one 16-byte transfer for 4-bit codes,
 // else one 4-byte transfer per code dword.
 __device__ __forceinline__ constexpr int dma_ops(int B) { return B == 4 ? 1 : B; }
