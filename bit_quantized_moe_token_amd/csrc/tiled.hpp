@@ -169,17 +169,25 @@ struct TKLoop {
     const uint32_t *zz = reinterpret_cast<const uint32_t *>(m + 256);
     t0.sc = sc[r]; t1.sc = sc[16 + r]; t2.sc = sc[32 + r]; t3.sc = sc[48 + r];
     t0.zz = zz[r]; t1.zz = zz[16 + r]; t2.zz = zz[32 + r]; t3.zz = zz[48 + r];
+    // activation fragments double-buffered across steps: step j + 1's NT
+    // reads are in flight while step j is decoded and multiplied
+    f16x8 av[2][NT];
+#pragma unroll
+    for (int s = 0; s < NT; ++s) av[0][s] = tlds_a(a, s, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if (j < 3) {
+#pragma unroll
+        for (int s = 0; s < NT; ++s) av[(j + 1) & 1][s] = tlds_a(a, s, j + 1);
+      }
       const f16x8 w0 = tdecode<B0, GPT>(t0, j), w1 = tdecode<B0, GPT>(t1, j);
       const f16x8 w2 = tdecode<B1, GPT>(t2, j), w3 = tdecode<B1, GPT>(t3, j);
 #pragma unroll
       for (int s = 0; s < NT; ++s) {
-        const f16x8 av = tlds_a(a, s, j);
-        acc[0][s] = mfma16(av, w0, acc[0][s]);
-        acc[1][s] = mfma16(av, w1, acc[1][s]);
-        acc[2][s] = mfma16(av, w2, acc[2][s]);
-        acc[3][s] = mfma16(av, w3, acc[3][s]);
+        acc[0][s] = mfma16(av[j & 1][s], w0, acc[0][s]);
+        acc[1][s] = mfma16(av[j & 1][s], w1, acc[1][s]);
+        acc[2][s] = mfma16(av[j & 1][s], w2, acc[2][s]);
+        acc[3][s] = mfma16(av[j & 1][s], w3, acc[3][s]);
       }
     }
   }
