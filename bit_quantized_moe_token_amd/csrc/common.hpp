@@ -114,6 +114,22 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Buffer resource over [base, base + bytes) for the raw buffer loads below
+// (dword 3: the gfx9 default data format; offsets past `bytes` read zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer -> LDS transfer of SIZE (4 or 16) bytes per lane from
+// base + soff + voff (voff per lane, soff uniform): lane l's bytes land at
+// lds_base + l * SIZE.  Like lds_dma, untracked by the compiler.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
+  const auto l = (__attribute__((address_space(3))) void *)lds_base;
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ f16x8 pack_b(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(f16x8, v);

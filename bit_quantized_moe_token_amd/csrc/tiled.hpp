@@ -35,19 +35,27 @@ struct TTile {
   uint32_t zz;   // zero of group gi in byte gi
 };
 
-// Address of dword e of tile t of strip s for lane l: the int_word_offset
-// layout written as (uniform part) + l * (uniform lane stride), so that the
-// full/ragged group choice is a scalar select.
+// Offset of dword e of tile t of strip s for lane l in an INT code region:
+// the int_word_offset layout written as (uniform part) + l * (uniform lane
+// stride), so that the full/ragged group choice is a scalar select.
+struct WordOff {
+  uint32_t uni, lane;
+};
 template <int B>
-__device__ __forceinline__ const uint8_t *tile_word_ptr(const uint8_t *codes, int s, int t, int e, int n_kt) {
+__device__ __forceinline__ WordOff tile_word_off(int s, int t, int e, int n_kt) {
   const int lane = threadIdx.x & 63;
   const int g4 = t >> 2, tl = t & 3;
   const int c = std::min(4, n_kt - 4 * g4);
-  const uint64_t base = (uint64_t)s * n_kt * 256 * B + (uint64_t)g4 * 1024 * B;
+  const uint32_t base = (uint32_t)s * n_kt * 256 * B + (uint32_t)g4 * 1024 * B;
   const int d = tl * B + e;
   const int ls = c == 4 ? 16 : c * 4 * B;
   const int ts = c == 4 ? (d >> 2) * 1024 + (d & 3) * 4 : tl * 4 * B + e * 4;
-  return codes + base + ts + lane * ls;
+  return WordOff{base + (uint32_t)ts, (uint32_t)(lane * ls)};
+}
+
+// Bytes of an INT block's code region (b dwords per lane per tile).
+__device__ __forceinline__ uint32_t code_region_bytes(const BlockDesc &d) {
+  return (uint32_t)(d.N / kStripRows) * (uint32_t)(d.K / kTileK) * 256u * (uint32_t)d.bits;
 }
 
 // fp16 B operand s * (c - z) of step j of a tile.
@@ -68,8 +76,10 @@ __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
 // (128 token rows x 256 B, 16-byte slots XOR-swizzled by row so that the
 // MFMA operand reads are bank-conflict free), the packed codes of the
 // workgroup's 16 strips (1 KiB each) and their scales and zeros.  All of
-// it is written by the LDS-DMA form of the global load (global_load_lds):
-// the data never occupies registers, so tiles are fetched two ahead of the
+// it is written by the LDS forms of the loads (activations and codes:
+// buffer_load ... lds against buffer resources, i.e. a scalar base plus a
+// 32-bit lane offset; scales and zeros: global_load_lds): the data never
+// occupies registers, so tiles are fetched two ahead of the
 // MFMAs through three stages, and the only memory counter the loop waits
 // on is the one for these transfers (explicit waits: the compiler does not
 // track DMA writes into LDS).
@@ -84,12 +94,16 @@ constexpr int kTStages = 3;
 __device__ __forceinline__ constexpr int dma_ops(int B) { return B == 4 ? 1 : B; }
 
 template <int B>
-__device__ __forceinline__ void dma_codes(const BlockDesc &d, int strip, int t, int n_kt, uint8_t *dst) {
+__device__ __forceinline__ void dma_codes(__amdgpu_buffer_rsrc_t codes, int strip, int t, int n_kt, uint8_t *dst) {
   if constexpr (B == 4) {
-    lds_dma<16>(tile_word_ptr<4>(d.codes, strip, t, 0, n_kt), dst);
+    const WordOff o = tile_word_off<4>(strip, t, 0, n_kt);
+    lds_dma_buf<16>(codes, o.lane, o.uni, dst);
   } else {
 #pragma unroll
-    for (int e = 0; e < B; ++e) lds_dma<4>(tile_word_ptr<B>(d.codes, strip, t, e, n_kt), dst + 256 * e);
+    for (int e = 0; e < B; ++e) {
+      const WordOff o = tile_word_off<B>(strip, t, e, n_kt);
+      lds_dma_buf<4>(codes, o.lane, o.uni, dst + 256 * e);
+    }
   }
 }
 
@@ -121,9 +135,9 @@ struct TKLoop {
   const BlockDesc &d0, &d1;
   const int *strips;
   int n_kt, wave;
-  const uint16_t *src;
   const uint32_t *rowoff;
   uint8_t *lds;
+  __amdgpu_buffer_rsrc_t ra, rc0, rc1;   // activations, codes of d0 and of d1
 
   __device__ __forceinline__ uint8_t *stage(int st) const { return lds + st * kTStageBytes; }
 
@@ -132,17 +146,18 @@ struct TKLoop {
   __device__ __forceinline__ void issue(int t, int st) const {
     const int lane = threadIdx.x & 63;
     uint8_t *a = stage(st);
+    // buffer loads: uniform tile offset + loop-invariant 32-bit lane offset
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 32 * wave + 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 15);
-      lds_dma<16>(src + rowoff[i] + t * kTileK + 8 * c, a + (32 * wave + 4 * i) * 256);
+      const uint32_t c = (uint32_t)((lane & 15) ^ (row & 15));
+      lds_dma_buf<16>(ra, 2u * (rowoff[i] + 8u * c), (uint32_t)t * (kTileK * 2), a + (32 * wave + 4 * i) * 256);
     }
     uint8_t *b = stage(st) + kTABytes + 4 * wave * 1024;
-    dma_codes<B0>(d0, strips[0], t, n_kt, b);
-    dma_codes<B0>(d0, strips[1], t, n_kt, b + 1024);
-    dma_codes<B1>(d1, strips[2], t, n_kt, b + 2048);
-    dma_codes<B1>(d1, strips[3], t, n_kt, b + 3072);
+    dma_codes<B0>(rc0, strips[0], t, n_kt, b);
+    dma_codes<B0>(rc0, strips[1], t, n_kt, b + 1024);
+    dma_codes<B1>(rc1, strips[2], t, n_kt, b + 2048);
+    dma_codes<B1>(rc1, strips[3], t, n_kt, b + 3072);
     // lane l: strip q = l / 16, row l % 16
     const int q = lane >> 4;
     const BlockDesc &dq = q < 2 ? d0 : d1;
@@ -248,7 +263,16 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const TKLoop<BG, BU, GPT> kl{dg, du, strips, a.H / kTileK, wave, a.x, rowoff, lds};
+  const TKLoop<BG, BU, GPT> kl{dg,
+                               du,
+                               strips,
+                               a.H / kTileK,
+                               wave,
+                               rowoff,
+                               lds,
+                               make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * 2u),
+                               make_rsrc(dg.codes, code_region_bytes(dg)),
+                               make_rsrc(du.codes, code_region_bytes(du))};
   kl.template run<8>(acc);
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
@@ -311,7 +335,9 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const TKLoop<BD, BD, GPT> kl{d, d, strips, a.I / kTileK, wave, a.h, rowoff, lds};
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.codes, code_region_bytes(d));
+  const TKLoop<BD, BD, GPT> kl{d, d, strips, a.I / kTileK, wave, rowoff, lds,
+                               make_rsrc(a.h, (uint32_t)a.P * (uint32_t)a.I * 2u), rc, rc};
   kl.template run<8>(acc);
   if (a.comp_on) {
     uint16_t *zs = reinterpret_cast<uint16_t *>(lds);
