@@ -58,7 +58,10 @@ def parse():
                    help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, "
                         "WRITE_SIZE) of a --copy-calibration run and record the scaled "
                         "per-launch HBM traffic of each kernel of the workload")
-    p.add_argument("--no-extra", action="store_true", help="skip the extra prefill measurement")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the extra measurements (prefill layer and the other three layers)")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the tiny, fine-grained and bit-plane layers (keep the prefill one)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph instead of launching it directly")
     return p.parse_args()
@@ -417,6 +420,25 @@ def main():
                               mfma_frac=palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
                               expert_counts=palg["counts"], kernels=pk)
     del layers
+    if args.workload == "decode" and not args.no_extra and not args.no_others:
+        # the other three layers of the workload set, measured the same way
+        # (cold weights: enough packed copies that the last-level cache
+        # cannot hold them), as context for the decode line
+        out["other_configs"] = {}
+        for short, R in (("tiny", 2), ("finegrained", 5), ("bitplane", 4)):
+            ocfg = configs.get(short)
+            olayers = build_layers(ocfg, args.seed, {"main": R}, {"main": ocfg})["main"]
+            oms, oprof, oalg = run_workload(ocfg, olayers, args.seed, max(20, args.steps // 4),
+                                            max(5, args.warmup // 4), args.path, graph=args.graph)
+            ok = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in oprof.items()}
+            out["other_configs"][short] = dict(
+                workload=ocfg["name"], ms_per_step=oms, tokens_s=ocfg["T"] / (oms * 1e-3),
+                alg_bytes=oalg["bytes"], alg_flops=oalg["flops"], active_experts=oalg["active"],
+                hbm_frac=oalg["bytes"] / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                mfma_frac=oalg["flops"] / (oms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                weight_copies=R, kernels=ok)
+            del olayers
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         # decode: the whole 16-token batch, repeated for about 12 s
         out["cpu_baseline"] = cpu_baseline(cfg, args.seed, min(cfg["T"], 16))

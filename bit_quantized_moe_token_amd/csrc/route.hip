@@ -307,11 +307,13 @@ route_mass_kernel(const float *__restrict__ gates, const int32_t *__restrict__ o
 
 using namespace moeq;
 
-// One segment: the single-workgroup kernel; more: per-segment counts in
-// the workspace.
+// Up to kRouteSingleMax tokens: the single-workgroup kernel (one launch;
+// its waves take the tokens in turn); more: segments, with per-segment
+// counts in the workspace.
+constexpr int kRouteSingleMax = 64;
+static inline bool route_single(int T) { return T <= kRouteSingleMax; }
 static inline size_t route_ws_bytes(int T, int E) {
-  const int nseg = route_segments(T);
-  return nseg > 1 ? (size_t)nseg * E * sizeof(int32_t) : 0;
+  return route_single(T) ? 0 : (size_t)route_segments(T) * E * sizeof(int32_t);
 }
 
 MOEQ_API moeq_status moeq_route_workspace_size(int32_t T, int32_t E, int32_t k, size_t *bytes) {
@@ -337,7 +339,7 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
     return fail(MOEQ_ERR_WORKSPACE, "route: workspace has %zu bytes, needs %zu", ws_bytes, need);
   prof_begin("route", stream);
   const int nseg = route_segments(T);
-  if (nseg <= 1) {
+  if (route_single(T)) {
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, logits, T, E, k,
                        out->topk_ids, out->topk_gates, out->expert_offsets, out->sorted_pairs,
                        out->pair_pos);

@@ -65,6 +65,7 @@ def test_route_validation(L):
     assert L.moeq_route_workspace_size(16, 8, 2, ctypes.byref(n)) == 0 and n.value == 0
     # more than 64 tokens: per-64-token-segment counts, E int32 each
     assert L.moeq_route_workspace_size(4096, 8, 2, ctypes.byref(n)) == 0 and n.value == 64 * 8 * 4
+    assert L.moeq_route_workspace_size(64, 128, 8, ctypes.byref(n)) == 0 and n.value == 0
     assert L.moeq_route_workspace_size(65, 128, 8, ctypes.byref(n)) == 0 and n.value == 2 * 128 * 4
     # workspace missing or too small: rejected before anything is enqueued
     assert L.moeq_route(ctypes.c_void_p(16), 4096, 8, 2, ctypes.byref(r), None, 0, None) == 3
