@@ -612,10 +612,14 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
   return moeq_dyn_lds;
 }
 
-// Chunk classes: NSUB = 1, 2, 4 token tiles (<= 16, <= 32, <= 64 tokens).
-// One launch per class present; a workgroup whose chunk is of another class
+// Chunk classes by token tiles: NSUB = 1 when no chunk can exceed 16
+// tokens, else 2 (up to 32 tokens, the smaller chunks included: one launch
+// fewer costs less than their idle MFMA rows) and 4 (up to 64).  One
+// launch per class present; a workgroup whose chunk is of another class
 // exits at once.
-__device__ __forceinline__ int nsub_of(int cnt) { return cnt <= 16 ? 1 : (cnt <= 32 ? 2 : 4); }
+__device__ __forceinline__ int class_of(int cnt, int nsub_max) {
+  return nsub_max == 1 ? 1 : (cnt <= 32 ? 2 : 4);
+}
 
 // LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
 inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
@@ -631,7 +635,7 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) gate
   const int n_sg = a.I / 64;
   const int chunk = blockIdx.x / n_sg, sg = blockIdx.x % n_sg;
   Chunk ch;
-  if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || class_of(ch.cnt, a.nsub_max) != NSUB) return;
   const int strip = 4 * sg + wave;
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
@@ -656,7 +660,7 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) down
   const int rest = blockIdx.x / a.splits;
   const int chunk = rest / n_sg, sg = rest % n_sg;
   Chunk ch;
-  if (!find_chunk(a.offsets, a.E, chunk, &ch) || nsub_of(ch.cnt) != NSUB) return;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || class_of(ch.cnt, a.nsub_max) != NSUB) return;
   switch (a.desc[3 * ch.e + 2].bits) {
     case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, sg, split, lds); break;
     case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, sg, split, lds); break;
@@ -667,8 +671,9 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) down
 // Launch helpers for one (GPT, PLANE) class, instantiated in the .hip files.
 template <int GPT, bool PLANE>
 void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
-  if (a.nsub_max >= 2)
+  if (a.nsub_max == 1)
+    hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
+  else
     hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
   if (a.nsub_max >= 3)
     hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
@@ -676,8 +681,9 @@ void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
 
 template <int GPT, bool PLANE>
 void launch_down_class(const FfnArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
-  if (a.nsub_max >= 2)
+  if (a.nsub_max == 1)
+    hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
+  else
     hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
   if (a.nsub_max >= 3)
     hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
