@@ -1,6 +1,7 @@
 // Top-k routing and the token -> expert counting sort: in one workgroup for
-// up to 64 tokens, else in 64-token segments (per-segment counts, then
-// offsets and placement per segment).
+// up to 64 tokens; else top-k in workgroups of 4 tokens, then placement in
+// 64-token segments (each segment counts every pair's expert itself, so
+// no workspace and no grid-wide step are needed).
 //
 // Top-k with softmax gates over the selected logits (router-guided top-n
 // compensation, "Bandwidth-Efficient Adaptive Mixture-of-Experts via
@@ -24,6 +25,7 @@ namespace moeq {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxE = 256;
+constexpr int kRouteTokens = 64;   // most tokens of the single-workgroup kernel
 
 struct Cand {
   float v;
@@ -34,39 +36,66 @@ __device__ __forceinline__ Cand better(Cand a, Cand b) {
   return (a.v > b.v || (a.v == b.v && a.id < b.id)) ? a : b;
 }
 
-__device__ __forceinline__ Cand wave_argmax(Cand c) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Cand o;
-    o.v = __shfl_xor(c.v, off, kWave);
-    o.id = __shfl_xor(c.id, off, kWave);
-    c = better(c, o);
-  }
-  return c;
+// c against its partner lane under one DPP lane permutation (ctrl: a DPP
+// control constant; every lane of a row is a valid source).
+template <int CTRL>
+__device__ __forceinline__ Cand dpp_better(Cand c) {
+  Cand o;
+  o.v = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, c.v), CTRL, 0xf, 0xf, true));
+  o.id = __builtin_amdgcn_mov_dpp(c.id, CTRL, 0xf, 0xf, true);
+  return better(c, o);
 }
 
-// Top-k of token t by one wave: k rounds of a wave-wide argmax, gates in
-// fp32; lane 0 writes ids (and counts them in an LDS histogram if given).
-__device__ __forceinline__ void topk_token(const float *__restrict__ logits, int t, int E, int k,
-                                           int32_t *__restrict__ ids, float *__restrict__ gates,
-                                           int *s_hist) {
+// Wave-wide best candidate, the same in every lane.  `better` is a total
+// order on (value desc, id asc), so the result does not depend on the
+// reduction tree: within each 16-lane row by DPP exchanges (quad swaps,
+// then half-row and row mirrors: every lane ends with its row's best),
+// then across the four rows through their first lanes.
+__device__ __forceinline__ Cand wave_argmax(Cand c) {
+  c = dpp_better<0xb1>(c);    // quad_perm [1,0,3,2]
+  c = dpp_better<0x4e>(c);    // quad_perm [2,3,0,1]
+  c = dpp_better<0x141>(c);   // row_half_mirror
+  c = dpp_better<0x140>(c);   // row_mirror
+  Cand r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[q].v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 16 * q));
+    r[q].id = __builtin_amdgcn_readlane(c.id, 16 * q);
+  }
+  return better(better(r[0], r[1]), better(r[2], r[3]));
+}
+
+constexpr int kSlots = kMaxE / kWave;   // logits (and selected slots) per lane
+
+// Logits of token t: lane l holds experts l + 64 s.
+__device__ __forceinline__ void load_logits(const float *__restrict__ logits, int t, int E, float *v) {
   const int lane = threadIdx.x & 63;
   const float *row = logits + (int64_t)t * E;
-  float v[kMaxE / kWave];
-  uint32_t taken = 0;
 #pragma unroll
-  for (int s = 0; s < kMaxE / kWave; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     const int e = lane + s * kWave;
     v[s] = e < E ? row[e] : 0.0f;
   }
+}
+
+// Top-k of token t by one wave from its logits v: k rounds of a wave-wide
+// argmax, gates in fp32.  The selected ids and logits stay in registers
+// (slot j with lane j % 64) until all rounds are done, so no round waits
+// for memory; then lanes j < k write slot j (and count it in the LDS
+// histogram if given).
+__device__ __forceinline__ void topk_token(const float *v, int t, int E, int k, int32_t *__restrict__ ids,
+                                           float *__restrict__ gates, int *s_hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t taken = 0;
   float top0 = 0.0f, denom = 0.0f;
-  float sel[kMaxE / kWave];   // logit of slot j kept by lane j % 64
+  float sel[kSlots];   // logit of slot j kept by lane j % 64
+  int sid[kSlots];     // its expert id
 #pragma unroll
-  for (int s = 0; s < kMaxE / kWave; ++s) sel[s] = 0.0f;
+  for (int s = 0; s < kSlots; ++s) { sel[s] = 0.0f; sid[s] = 0; }
   for (int j = 0; j < k; ++j) {
     Cand c{-__builtin_inff(), 0x7fffffff};
 #pragma unroll
-    for (int s = 0; s < kMaxE / kWave; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       const int e = lane + s * kWave;
       if (e < E && !((taken >> s) & 1u)) c = better(c, Cand{v[s], e});
     }
@@ -74,17 +103,35 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
     if ((c.id & 63) == lane) taken |= 1u << (c.id >> 6);
     if (j == 0) top0 = c.v;
     denom += __expf(c.v - top0);
-    if ((j & 63) == lane) sel[j >> 6] = c.v;
-    if (lane == 0) {
-      ids[(int64_t)t * k + j] = c.id;
-      if (s_hist) atomicAdd(&s_hist[c.id], 1);
-    }
+    if ((j & 63) == lane) { sel[j >> 6] = c.v; sid[j >> 6] = c.id; }
   }
 #pragma unroll
-  for (int s = 0; s < kMaxE / kWave; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     const int j = lane + s * kWave;
-    if (j < k) gates[(int64_t)t * k + j] = __expf(sel[s] - top0) / denom;
+    if (j < k) {
+      ids[(int64_t)t * k + j] = sid[s];
+      gates[(int64_t)t * k + j] = __expf(sel[s] - top0) / denom;
+      if (s_hist) atomicAdd(&s_hist[sid[s]], 1);
+    }
   }
+}
+
+// Tokens t0 + i * step < t1 (i < NT) by one wave: every token's logits
+// are requested first, so the wave waits for memory once, not per token
+// and not per round.
+template <int NT>
+__device__ __forceinline__ void topk_tokens(const float *__restrict__ logits, int t0, int t1, int step, int E, int k,
+                                            int32_t *__restrict__ ids, float *__restrict__ gates, int *s_hist) {
+  float v[NT][kSlots];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+    if (t0 + i * step < t1) load_logits(logits, t0 + i * step, E, v[i]);
+  // all loads done here: the compiler then knows that no later wait is
+  // needed (it would otherwise wait on each token's stores)
+  vm_wait<0>();
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+    if (t0 + i * step < t1) topk_token(v[i], t0 + i * step, E, k, ids, gates, s_hist);
 }
 
 __global__ void __launch_bounds__(kRouteThreads)
@@ -100,7 +147,7 @@ route_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__r
   for (int e = tid; e < kMaxE; e += kRouteThreads) { s_count[e] = 0; s_run[e] = 0; }
 
   // ---- phase 1: top-k + gates, one wave per token
-  for (int t = wave; t < T; t += kRouteWaves) topk_token(logits, t, E, k, ids, gates, nullptr);
+  topk_tokens<kRouteTokens / kRouteWaves>(logits, wave, T, kRouteWaves, E, k, ids, gates, nullptr);
   __syncthreads();
 
   // ---- phase 2: histogram + exclusive scan
@@ -163,35 +210,32 @@ route_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__r
 }
 
 
-// ---- many tokens: segments of kSegTokens tokens, two kernels.
+// ---- many tokens: two kernels.  Top-k spread over workgroups of
+// kTopkWaves tokens (one wave per token, one wave per SIMD), so the
+// rounds of many tokens run on many CUs; then placement in segments of
+// kSegTokens tokens.
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kSegThreads = 256;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kSegTokens = 64;
+static_assert(kRouteTokens % kRouteWaves == 0, "each wave takes the same number of tokens");
 
-// Segment blockIdx.x: top-k of its tokens (16 waves, one per token) and
-// its per-expert pair counts seg_count[seg][e].
-__global__ void __launch_bounds__(kRouteThreads)
+__global__ void __launch_bounds__(kTopkThreads)
 route_topk_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
-                  float *__restrict__ gates, int32_t *__restrict__ seg_count) {
-  __shared__ int s_hist[kMaxE];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int e = tid; e < kMaxE; e += kRouteThreads) s_hist[e] = 0;
-  __syncthreads();
-  const int t0 = blockIdx.x * kSegTokens, t1 = std::min(T, t0 + kSegTokens);
-  for (int t = t0 + wave; t < t1; t += kRouteWaves) topk_token(logits, t, E, k, ids, gates, s_hist);
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) seg_count[(int64_t)blockIdx.x * E + e] = s_hist[e];
+                  float *__restrict__ gates) {
+  const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+  topk_tokens<1>(logits, t, T, kTopkWaves, E, k, ids, gates, nullptr);
 }
 
-// Segment blockIdx.x: expert offsets from every segment's counts (segment 0
-// writes them), this segment's first slot per expert (pairs of earlier
-// segments come first), then the stable placement of its pairs in
-// ascending pair id (ballot peer masks inside a wave, per-wave counts
-// across waves and chunks).
+// Segment blockIdx.x: per-expert pair totals and the counts of the pairs
+// before the segment, from all T*k expert ids (LDS counters); expert
+// offsets by an exclusive scan (segment 0 writes them); then the stable
+// placement of the segment's pairs in ascending pair id (ballot peer masks
+// inside a wave, per-wave counts across waves and chunks).
 __global__ void __launch_bounds__(kSegThreads)
-route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, const int32_t *__restrict__ seg_count,
-                   int nseg, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pairs,
-                   int32_t *__restrict__ pair_pos) {
+route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
+                   int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ pair_pos) {
   __shared__ int s_tot[kMaxE];
   __shared__ int s_base[kMaxE];
   __shared__ int s_off[kMaxE + 1];
@@ -199,17 +243,15 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, const i
   __shared__ int s_wave[kSegWaves][kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = blockIdx.x;
-  for (int e = tid; e < E; e += kSegThreads) {
-    int tot = 0, before = 0;
-#pragma unroll 8
-    for (int g = 0; g < nseg; ++g) {
-      const int c = seg_count[(int64_t)g * E + e];
-      tot += c;
-      before += g < seg ? c : 0;
-    }
-    s_tot[e] = tot;
-    s_base[e] = before;
-    s_run[e] = 0;
+  const int P = T * k;
+  const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
+  for (int e = tid; e < E; e += kSegThreads) { s_tot[e] = 0; s_base[e] = 0; s_run[e] = 0; }
+  __syncthreads();
+#pragma unroll 4
+  for (int p = tid; p < P; p += kSegThreads) {
+    const int e = ids[p];
+    atomicAdd(&s_tot[e], 1);
+    if (p < p0) atomicAdd(&s_base[e], 1);
   }
   __syncthreads();
   if (wave == 0) {
@@ -233,7 +275,6 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, const i
     for (int e = tid; e <= E; e += kSegThreads) offsets[e] = s_off[e];
   for (int e = tid; e < E; e += kSegThreads) s_base[e] += s_off[e];
   __syncthreads();
-  const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
   for (int base = p0; base < p1; base += kSegThreads) {
     const int p = base + tid;
     const bool valid = p < p1;
@@ -308,13 +349,11 @@ route_mass_kernel(const float *__restrict__ gates, const int32_t *__restrict__ o
 using namespace moeq;
 
 // Up to kRouteSingleMax tokens: the single-workgroup kernel (one launch;
-// its waves take the tokens in turn); more: segments, with per-segment
-// counts in the workspace.
-constexpr int kRouteSingleMax = 64;
+// its waves take the tokens in turn); more: the top-k and placement
+// kernels.  Neither needs a workspace.
+constexpr int kRouteSingleMax = kRouteTokens;
 static inline bool route_single(int T) { return T <= kRouteSingleMax; }
-static inline size_t route_ws_bytes(int T, int E) {
-  return route_single(T) ? 0 : (size_t)route_segments(T) * E * sizeof(int32_t);
-}
+static inline size_t route_ws_bytes(int, int) { return 0; }
 
 MOEQ_API moeq_status moeq_route_workspace_size(int32_t T, int32_t E, int32_t k, size_t *bytes) {
   if (!bytes) return fail(MOEQ_ERR_INVALID, "route_workspace_size: null output");
@@ -344,11 +383,10 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
                        out->topk_ids, out->topk_gates, out->expert_offsets, out->sorted_pairs,
                        out->pair_pos);
   } else {
-    int32_t *cnt = static_cast<int32_t *>(ws);
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nseg), dim3(kRouteThreads), 0, stream, logits, T, E, k,
-                       out->topk_ids, out->topk_gates, cnt);
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkThreads), 0, stream,
+                       logits, T, E, k, out->topk_ids, out->topk_gates);
     hipLaunchKernelGGL(route_place_kernel, dim3(nseg), dim3(kSegThreads), 0, stream, out->topk_ids, T, E, k,
-                       cnt, nseg, out->expert_offsets, out->sorted_pairs, out->pair_pos);
+                       out->expert_offsets, out->sorted_pairs, out->pair_pos);
   }
   prof_end("route", stream);
   return check_launch("route");

@@ -265,8 +265,8 @@ moeq_status moeq_route_workspace_size(int32_t T, int32_t E, int32_t k, size_t *b
  * uneven expert activation.)
  *   logits DEVICE [T, E] fp32, finite.  T >= 0, 1 <= k <= E <= 256.
  *   ws DEVICE workspace of at least moeq_route_workspace_size bytes
- *   (may be NULL when that size is 0; it is when T <= 64); a smaller one
- *   returns MOEQ_ERR_WORKSPACE.
+ *   (may be NULL when that size is 0, which it is for every T in this
+ *   version); a smaller one returns MOEQ_ERR_WORKSPACE.
  */
 moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32_t k,
                        const moeq_routing *out, void *ws, size_t ws_bytes,

@@ -61,16 +61,13 @@ def test_route_validation(L):
     assert L.moeq_route(ctypes.c_void_p(16), 4, 8, 9, ctypes.byref(r), None, 0, None) == 1
     assert L.moeq_route(ctypes.c_void_p(16), 4, 300, 2, ctypes.byref(r), None, 0, None) == 1
     assert L.moeq_route(ctypes.c_void_p(16), -1, 8, 2, ctypes.byref(r), None, 0, None) == 1
+    # neither the single-workgroup path (T <= 64) nor the two-kernel path
+    # (each placement segment counts all pairs itself) needs a workspace
+    for T, E, k in [(16, 8, 2), (64, 128, 8), (65, 128, 8), (4096, 8, 2), (1 << 20, 256, 8)]:
+        n = ctypes.c_size_t(7)
+        assert L.moeq_route_workspace_size(T, E, k, ctypes.byref(n)) == 0 and n.value == 0
     n = ctypes.c_size_t(7)
-    assert L.moeq_route_workspace_size(16, 8, 2, ctypes.byref(n)) == 0 and n.value == 0
-    # more than 64 tokens: per-64-token-segment counts, E int32 each
-    assert L.moeq_route_workspace_size(4096, 8, 2, ctypes.byref(n)) == 0 and n.value == 64 * 8 * 4
-    assert L.moeq_route_workspace_size(64, 128, 8, ctypes.byref(n)) == 0 and n.value == 0
-    assert L.moeq_route_workspace_size(65, 128, 8, ctypes.byref(n)) == 0 and n.value == 2 * 128 * 4
-    # workspace missing or too small: rejected before anything is enqueued
-    assert L.moeq_route(ctypes.c_void_p(16), 4096, 8, 2, ctypes.byref(r), None, 0, None) == 3
-    assert L.moeq_route(ctypes.c_void_p(16), 4096, 8, 2, ctypes.byref(r), ctypes.c_void_p(16), 64 * 8 * 4 - 1,
-                        None) == 3
+    assert L.moeq_route_workspace_size(16, 8, 9, ctypes.byref(n)) == 1 and n.value == 7
 
 
 def test_route_mass_validation_cpu(L):
