@@ -17,6 +17,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -242,6 +243,37 @@ KERNEL_KEYS = [("gateup_kernel", "gateup_stream"), ("down_kernel", "down_stream"
                ("route", "route"), ("combine", "combine"), ("neg_kernel", "calibration_copy")]
 
 
+def hbm_context(reps=10):
+    """Plain torch streaming kernels over 1 GiB (a read-only sum and a copy),
+    timed with events on torch's stream: what simple streaming code reaches
+    on this GPU, as context for the HBM fractions (the peak stays 8 TB/s)."""
+    import torch
+    n = 1 << 28                                    # 1 GiB of fp32
+    a = torch.full((n,), 1.0, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+
+    def med(fn):
+        ts = []
+        for i in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(ts)
+
+    t_read = med(lambda: a.sum())
+    t_copy = med(lambda: b.copy_(a))
+    del a, b
+    torch.cuda.empty_cache()
+    read = (n * 4) / t_read / 1e9
+    copy = (2 * n * 4) / t_copy / 1e9
+    return dict(read_GBps=read, read_frac=read / HBM_PEAK_GBS, copy_GBps=copy, copy_frac=copy / HBM_PEAK_GBS,
+                bytes=n * 4, what="torch sum (read) and copy_ (read + write) of 1 GiB fp32, median of %d" % reps)
+
+
 def _read_pmc(folder, counter):
     """Per-kernel list of per-dispatch values of `counter` (KiB) from the
     counter_collection.csv files under `folder`."""
@@ -271,7 +303,6 @@ def _read_pmc(folder, counter):
 
 
 def summarize_pmc(workload, fetch_dir, write_dir):
-    import statistics
     fe = _read_pmc(fetch_dir, "FETCH_SIZE")
     wr = _read_pmc(write_dir, "WRITE_SIZE")
     # each counter is scaled by what it reads for the copy of CALIB_BYTES
@@ -439,6 +470,8 @@ def main():
                 weight_copies=R, kernels=ok)
             del olayers
             torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_extra:
+        out["hbm_context"] = hbm_context()
     if not args.no_cpu_baseline:
         # decode: the whole 16-token batch, repeated for about 12 s
         out["cpu_baseline"] = cpu_baseline(cfg, args.seed, min(cfg["T"], 16))

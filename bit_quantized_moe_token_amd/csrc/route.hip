@@ -1,5 +1,5 @@
 // Top-k routing and the token -> expert counting sort: in one workgroup for
-// up to 64 tokens; else top-k in workgroups of 4 tokens, then placement in
+// up to 16 tokens; else top-k in workgroups of 4 tokens, then placement in
 // 64-token segments (each segment counts every pair's expert itself, so
 // no workspace and no grid-wide step are needed).
 //
@@ -25,7 +25,7 @@ namespace moeq {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxE = 256;
-constexpr int kRouteTokens = 64;   // most tokens of the single-workgroup kernel
+constexpr int kRouteTokens = 16;   // most tokens of the single-workgroup kernel: one per wave
 
 struct Cand {
   float v;
@@ -348,9 +348,10 @@ route_mass_kernel(const float *__restrict__ gates, const int32_t *__restrict__ o
 
 using namespace moeq;
 
-// Up to kRouteSingleMax tokens: the single-workgroup kernel (one launch;
-// its waves take the tokens in turn); more: the top-k and placement
-// kernels.  Neither needs a workspace.
+// Up to kRouteSingleMax tokens: the single-workgroup kernel (one launch,
+// one wave per token); more: the top-k and placement kernels (measured:
+// 9.7 against 11.9 us at 64 tokens, 9.4 against 7.8 us at 16).  Neither
+// needs a workspace.
 constexpr int kRouteSingleMax = kRouteTokens;
 static inline bool route_single(int T) { return T <= kRouteSingleMax; }
 static inline size_t route_ws_bytes(int, int) { return 0; }
