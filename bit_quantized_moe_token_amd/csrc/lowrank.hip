@@ -91,26 +91,55 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   }
 }
 
-// y[t] = sum_j g[t][j] * sum_s ypart[s][pair_pos[t*k+j]]; one thread per
-// (token, 4 columns).
-template <bool F32>
+// y[t] = sum_j g[t][j] * sum_s ypart[s][pair_pos[t*k+j]], slots in order,
+// splits in order within a slot; one thread per (token, 4 columns).  Slots
+// go in groups of 4: their gates and positions are loaded together, then
+// every partial of the group (up to MS splits each; MS = 1 when there is
+// one split, so that the many-token case keeps few registers) is requested
+// before the first add, so a group costs two memory round trips, not one
+// per partial.
+template <bool F32, int MS>
 __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int per_t = a.H / 4;
   if (id >= (int64_t)a.T * per_t) return;
   const int t = (int)(id / per_t), c = (int)(id % per_t) * 4;
+  const int64_t tk = (int64_t)t * a.k;
+  const int ns = a.splits;
   f32x4 out = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) {
-    const float g = a.gates[(int64_t)t * a.k + j];
-    const int pos = a.pair_pos[(int64_t)t * a.k + j];
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.splits; ++s) {
-      const f32x4 p = *reinterpret_cast<const f32x4 *>(a.ypart + ((int64_t)s * a.P + pos) * a.H + c);
+  for (int j0 = 0; j0 < a.k; j0 += 4) {
+    float g[4];
+    int pos[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] += p[q];
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool ok = j0 + jj < a.k;
+      g[jj] = ok ? a.gates[tk + j0 + jj] : 0.f;
+      pos[jj] = ok ? a.pair_pos[tk + j0 + jj] : 0;
     }
+    f32x4 v[4][MS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = __builtin_fmaf(g, v[q], out[q]);
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int s = 0; s < MS; ++s)
+        if (j0 + jj < a.k && s < ns)
+          v[jj][s] = *reinterpret_cast<const f32x4 *>(a.ypart + ((int64_t)s * a.P + pos[jj]) * a.H + c);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (j0 + jj >= a.k) break;
+      f32x4 sum = v[jj][0];
+#pragma unroll
+      for (int s = 1; s < MS; ++s)
+        if (s < ns)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum[q] += v[jj][s][q];
+      for (int s = MS; s < ns; ++s) {
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(a.ypart + ((int64_t)s * a.P + pos[jj]) * a.H + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += p[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = __builtin_fmaf(g[jj], sum[q], out[q]);
+    }
   }
   if (F32) {
     *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + (int64_t)t * a.H + c) = out;
@@ -131,8 +160,13 @@ void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s) {
   const int64_t n = (int64_t)a.T * (a.H / 4);
   const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (f32) hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, a, y);
-  else hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, a, y);
+  if (a.splits == 1) {
+    if (f32) hipLaunchKernelGGL((combine_kernel<true, 1>), dim3(blocks), dim3(256), 0, s, a, y);
+    else hipLaunchKernelGGL((combine_kernel<false, 1>), dim3(blocks), dim3(256), 0, s, a, y);
+  } else {
+    if (f32) hipLaunchKernelGGL((combine_kernel<true, 4>), dim3(blocks), dim3(256), 0, s, a, y);
+    else hipLaunchKernelGGL((combine_kernel<false, 4>), dim3(blocks), dim3(256), 0, s, a, y);
+  }
 }
 
 }  // namespace moeq
