@@ -81,10 +81,10 @@ __device__ __forceinline__ void load_logits(const float *__restrict__ logits, in
 // Top-k of token t by one wave from its logits v: k rounds of a wave-wide
 // argmax, gates in fp32.  The selected ids and logits stay in registers
 // (slot j with lane j % 64) until all rounds are done, so no round waits
-// for memory; then lanes j < k write slot j (and count it in the LDS
-// histogram if given).
+// for memory; then lanes j < k write slot j (and, if given, count it in
+// the LDS histogram and copy its id to LDS).
 __device__ __forceinline__ void topk_token(const float *v, int t, int E, int k, int32_t *__restrict__ ids,
-                                           float *__restrict__ gates, int *s_hist) {
+                                           float *__restrict__ gates, int *s_hist, int *s_ids) {
   const int lane = threadIdx.x & 63;
   uint32_t taken = 0;
   float top0 = 0.0f, denom = 0.0f;
@@ -112,6 +112,7 @@ __device__ __forceinline__ void topk_token(const float *v, int t, int E, int k, 
       ids[(int64_t)t * k + j] = sid[s];
       gates[(int64_t)t * k + j] = __expf(sel[s] - top0) / denom;
       if (s_hist) atomicAdd(&s_hist[sid[s]], 1);
+      if (s_ids) s_ids[t * k + j] = sid[s];
     }
   }
 }
@@ -121,7 +122,8 @@ __device__ __forceinline__ void topk_token(const float *v, int t, int E, int k, 
 // and not per round.
 template <int NT>
 __device__ __forceinline__ void topk_tokens(const float *__restrict__ logits, int t0, int t1, int step, int E, int k,
-                                            int32_t *__restrict__ ids, float *__restrict__ gates, int *s_hist) {
+                                            int32_t *__restrict__ ids, float *__restrict__ gates, int *s_hist,
+                                            int *s_ids = nullptr) {
   float v[NT][kSlots];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
@@ -131,7 +133,7 @@ __device__ __forceinline__ void topk_tokens(const float *__restrict__ logits, in
   vm_wait<0>();
 #pragma unroll
   for (int i = 0; i < NT; ++i)
-    if (t0 + i * step < t1) topk_token(v[i], t0 + i * step, E, k, ids, gates, s_hist);
+    if (t0 + i * step < t1) topk_token(v[i], t0 + i * step, E, k, ids, gates, s_hist, s_ids);
 }
 
 __global__ void __launch_bounds__(kRouteThreads)
@@ -142,18 +144,19 @@ route_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__r
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_run[kMaxE];
   __shared__ int s_wave[kRouteWaves][kMaxE];
+  __shared__ int s_ids[kRouteTokens * kMaxE];   // the pairs' expert ids
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < kMaxE; e += kRouteThreads) { s_count[e] = 0; s_run[e] = 0; }
-
-  // ---- phase 1: top-k + gates, one wave per token
-  topk_tokens<kRouteTokens / kRouteWaves>(logits, wave, T, kRouteWaves, E, k, ids, gates, nullptr);
   __syncthreads();
 
-  // ---- phase 2: histogram + exclusive scan
+  // ---- phase 1: top-k + gates, one wave per token; the histogram and the
+  // ids also go to LDS, so the later phases read nothing back from memory
+  topk_tokens<kRouteTokens / kRouteWaves>(logits, wave, T, kRouteWaves, E, k, ids, gates, s_count, s_ids);
+  __syncthreads();
+
+  // ---- phase 2: exclusive scan of the histogram
   const int P = T * k;
-  for (int p = tid; p < P; p += kRouteThreads) atomicAdd(&s_count[ids[p]], 1);
-  __syncthreads();
   if (wave == 0) {
     int carry = 0;
     for (int base = 0; base < E; base += kWave) {
@@ -177,7 +180,7 @@ route_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__r
   for (int base = 0; base < P; base += kRouteThreads) {
     const int p = base + tid;
     const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
+    const int e = valid ? s_ids[p] : 0;
     // lanes of this wave holding the same expert
     uint64_t peers = __ballot(valid);
 #pragma unroll
