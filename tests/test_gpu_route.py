@@ -44,7 +44,7 @@ def test_route_configs(name, seed):
 
 @pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 8), (5, 3, 1), (333, 256, 7), (70, 64, 64),
                                    (2000, 5, 2), (1030, 128, 8), (4096, 2, 2), (64, 8, 2), (65, 256, 256),
-                                   (129, 7, 3)])
+                                   (129, 7, 3), (16, 256, 256), (17, 8, 2), (16, 8, 2)])
 def test_route_shapes_and_ties(T, E, k):
     rng = np.random.default_rng(T + E + k)
     logits = (rng.integers(-2, 3, size=(T, E)) * 0.25).astype(np.float32)   # many ties
