@@ -34,6 +34,19 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const int R = set ? a.rs : a.r;
   const int K = d.K;
   const int KS = mode == 0 ? a.ks_gu : a.ks_d;
+  float *zbase = mode == 0 ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
+  const int zstride = mode == 0 ? 2 * a.RZ : a.RZ;
+  const int zcol = bi * a.RZ + set * a.Rp + 16 * it + (lane & 15);
+  if (16 * it >= R) {
+    // the whole tile is padding past the factor's rank: zero rows, no loads
+    if (wave == 0)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 16 * sub + 4 * (lane >> 4) + q;
+        if (m < ch.cnt) zbase[(int64_t)(ch.base + m) * zstride + zcol] = 0.0f;
+      }
+    return;
+  }
   const int i = 16 * it + (lane & 15);
   const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
   const int pos = ch.base + mloc;
@@ -78,15 +91,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
 #pragma unroll
     for (int q = 0; q < 4; ++q) sum[q] += p[q];
   }
-  float *zbase = mode == 0 ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
-  const int zstride = mode == 0 ? 2 * a.RZ : a.RZ;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 16 * sub + 4 * (lane >> 4) + q;
     if (m < ch.cnt) {
       const int p2 = ch.base + m;
       const bool comp = (a.sorted_pairs[p2] % a.k) < a.n_comp;
-      zbase[(int64_t)p2 * zstride + bi * a.RZ + set * a.Rp + 16 * it + (lane & 15)] = comp ? sum[q] : 0.0f;
+      zbase[(int64_t)p2 * zstride + zcol] = comp ? sum[q] : 0.0f;
     }
   }
 }
