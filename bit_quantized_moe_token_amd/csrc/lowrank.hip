@@ -12,84 +12,114 @@ namespace moeq {
 
 // Partial z[pos][slot] = V v over one K range for compensated pairs (zero
 // for the others); the consumer kernels sum the ks partials in fixed order.
-// One 16-token tile per workgroup, 4 waves split the range and reduce
-// through LDS in fixed order.
-// grid.x = max_chunks * 4 tiles, grid.y = (#blocks) * (Rp + Rsp) / 16,
+// One 16-token tile and NJ 16-column jobs per workgroup (NJ = 2 when many
+// tokens leave no K split: each activation fragment then feeds both jobs,
+// so the activations are read half as often); 4 waves split the range and
+// reduce through LDS in fixed order.
+// grid.x = max_chunks * 4 tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ,
 // grid.z = ks.  mode 0: v = x[token] (gate/up blocks); mode 1: v = h[pos]
 // (down block).
+template <int NJ>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode) {
-  __shared__ f32x4 s_part[4][64];
+  __shared__ f32x4 s_part[4][NJ][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int chunk = blockIdx.x / 4, sub = blockIdx.x % 4;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch)) return;
   if (16 * sub >= ch.cnt) return;
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
-  const int bi = blockIdx.y / jobs_per_blk, rem = blockIdx.y % jobs_per_blk;
-  const int set = rem < a.Rp / 16 ? 0 : 1;
-  const int it = set ? rem - a.Rp / 16 : rem;
-  const int blk = mode == 0 ? bi : 2;
-  const BlockDesc &d = a.desc[3 * ch.e + blk];
-  const uint16_t *V = set ? d.Vs : d.V;
-  const int R = set ? a.rs : a.r;
-  const int K = d.K;
+  const int K = mode == 0 ? a.H : a.I;
   const int KS = mode == 0 ? a.ks_gu : a.ks_d;
   float *zbase = mode == 0 ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
   const int zstride = mode == 0 ? 2 * a.RZ : a.RZ;
-  const int zcol = bi * a.RZ + set * a.Rp + 16 * it + (lane & 15);
-  if (16 * it >= R) {
-    // the whole tile is padding past the factor's rank: zero rows, no loads
+  int zcol[NJ];
+  bool live[NJ], vi[NJ];
+  const uint16_t *vrow[NJ];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int job = (int)blockIdx.y * NJ + j;
+    const int bi = job / jobs_per_blk, rem = job % jobs_per_blk;
+    const int set = rem < a.Rp / 16 ? 0 : 1;
+    const int it = set ? rem - a.Rp / 16 : rem;
+    const BlockDesc &d = a.desc[3 * ch.e + (mode == 0 ? bi : 2)];
+    const uint16_t *V = set ? d.Vs : d.V;
+    const int R = set ? a.rs : a.r;
+    zcol[j] = bi * a.RZ + set * a.Rp + 16 * it + (lane & 15);
+    // a job wholly in the rank padding (rank 8 or 16 padded to 32) loads
+    // nothing and writes zero rows
+    live[j] = 16 * it < R;
+    any = any || live[j];
+    const int i = 16 * it + (lane & 15);
+    vi[j] = live[j] && i < R;
+    vrow[j] = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
+  }
+  if (!any) {
     if (wave == 0)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = 16 * sub + 4 * (lane >> 4) + q;
-        if (m < ch.cnt) zbase[(int64_t)(ch.base + m) * zstride + zcol] = 0.0f;
+        if (m < ch.cnt)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) zbase[(int64_t)(ch.base + m) * zstride + zcol[j]] = 0.0f;
       }
     return;
   }
-  const int i = 16 * it + (lane & 15);
   const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
   const int pos = ch.base + mloc;
   const uint16_t *arow = (mode == 0) ? a.x + (int64_t)(a.sorted_pairs[pos] / a.k) * a.H
                                      : a.h + (int64_t)pos * a.I;
   arow += 8 * (lane >> 4);
-  const uint16_t *vrow = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
-  const bool vi = i < R;
   const int nsteps = K / 32;
   const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
   const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
-  // batches of 8 steps: all 16 fragment loads are issued before the first
-  // MFMA, so each batch waits for memory once
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+  // batches of BATCH steps: all their fragment loads are issued before the
+  // first MFMA, so each batch waits for memory once
+  constexpr int BATCH = 8 / NJ;
+  const f16x8 zero = pack_b(0, 0, 0, 0);
+  f32x4 acc[NJ], acc2[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) { acc[j] = f32x4{0.f, 0.f, 0.f, 0.f}; acc2[j] = acc[j]; }
   int st = s0;
-  for (; st + 8 <= s1; st += 8) {
-    f16x8 av[8], bv[8];
+  for (; st + BATCH <= s1; st += BATCH) {
+    f16x8 av[BATCH], bv[BATCH][NJ];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       av[u] = load_a(arow + 32 * (st + u));
-      bv[u] = vi ? load_a(vrow + 32 * (st + u)) : pack_b(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bv[u][j] = vi[j] ? load_a(vrow[j] + 32 * (st + u)) : zero;
     }
 #pragma unroll
-    for (int u = 0; u < 8; u += 2) {
-      acc = mfma16(av[u], bv[u], acc);
-      acc2 = mfma16(av[u + 1], bv[u + 1], acc2);
-    }
+    for (int u = 0; u < BATCH; u += 2)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[j] = mfma16(av[u], bv[u][j], acc[j]);
+        acc2[j] = mfma16(av[u + 1], bv[u + 1][j], acc2[j]);
+      }
   }
   for (; st < s1; ++st) {
-    const f16x8 b = vi ? load_a(vrow + 32 * st) : pack_b(0, 0, 0, 0);
-    acc = mfma16(load_a(arow + 32 * st), b, acc);
+    const f16x8 av = load_a(arow + 32 * st);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mfma16(av, vi[j] ? load_a(vrow[j] + 32 * st) : zero, acc[j]);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] += acc2[q];
-  s_part[wave][lane] = acc;
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[j][q] += acc2[j][q];
+    s_part[wave][j][lane] = acc[j];
+  }
   __syncthreads();
   if (wave != 0) return;
-  f32x4 sum = s_part[0][lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const f32x4 p = s_part[w][lane];
+  for (int j = 0; j < NJ; ++j) {
+    f32x4 sum = s_part[0][j][lane];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] += p[q];
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 p = s_part[w][j][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum[q] += p[q];
+    }
+    acc[j] = sum;
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -97,7 +127,9 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     if (m < ch.cnt) {
       const int p2 = ch.base + m;
       const bool comp = (a.sorted_pairs[p2] % a.k) < a.n_comp;
-      zbase[(int64_t)p2 * zstride + zcol] = comp ? sum[q] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        zbase[(int64_t)p2 * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
     }
   }
 }
@@ -165,7 +197,14 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
   grid.z = mode == 0 ? a.ks_gu : a.ks_d;
-  hipLaunchKernelGGL(lowrank_project_kernel, grid, dim3(256), 0, s, a, mode);
+  // two jobs per workgroup when many tokens leave no K split (the
+  // activation re-reads dominate); the job count is always even
+  if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) {
+    grid.y /= 2;
+    hipLaunchKernelGGL(lowrank_project_kernel<2>, grid, dim3(256), 0, s, a, mode);
+  } else {
+    hipLaunchKernelGGL(lowrank_project_kernel<1>, grid, dim3(256), 0, s, a, mode);
+  }
 }
 
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s) {
