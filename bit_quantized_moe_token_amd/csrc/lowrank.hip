@@ -197,9 +197,13 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
   grid.z = mode == 0 ? a.ks_gu : a.ks_d;
-  // two jobs per workgroup when many tokens leave no K split (the
-  // activation re-reads dominate); the job count is always even
-  if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) {
+  // two (four, from eight jobs up) jobs per workgroup when many tokens
+  // leave no K split (the activation re-reads dominate; fewer jobs keep
+  // enough workgroups); the job count is always even
+  if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) {
+    grid.y /= 4;
+    hipLaunchKernelGGL(lowrank_project_kernel<4>, grid, dim3(256), 0, s, a, mode);
+  } else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) {
     grid.y /= 2;
     hipLaunchKernelGGL(lowrank_project_kernel<2>, grid, dim3(256), 0, s, a, mode);
   } else {
