@@ -170,6 +170,23 @@ def time_steps(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def step_distribution(fn, steps):
+    """Per-step event pairs on torch's stream (the library launches on it):
+    median, p10 and p90 of the step time in ms, next to the block mean."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+
+    def q(f):
+        return ts[min(len(ts) - 1, int(f * len(ts)))]
+    return dict(median=statistics.median(ts), p10=q(0.1), p90=q(0.9), n=len(ts))
+
+
 def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, graph=False, split_k=0):
     import numpy as np
     import torch
@@ -207,6 +224,7 @@ def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, grap
             graphs[i % R].replay()
 
     ms = time_steps(timed, steps, warmup)
+    dist = step_distribution(timed, steps)
     prof = {}
     if profile:
         moeq.profile_enable(True)
@@ -219,6 +237,7 @@ def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, grap
     offsets = rt.offsets.cpu().numpy()
     sp = rt.sorted_pairs.cpu().numpy()
     alg = algorithmic(cfg, layers_list[0], offsets, sp, cfg["n_comp"])
+    alg["step_ms_dist"] = dist
     return ms, prof, alg
 
 
@@ -439,17 +458,18 @@ def main():
                       hbm_frac_step=alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       hbm_frac_kernels=(alg["bytes"] / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS) if ffn_us else None),
         "kernels": kern,
+        "step_ms_dist": alg["step_ms_dist"],
         "setup_s": setup_s,
     }
     if extra_cfg is not None:
-        pms, pprof, palg = run_workload(extra_cfg, layers["prefill"], args.seed, max(3, args.steps // 20),
-                                        max(1, args.warmup // 10), args.path, graph=args.graph)
+        pms, pprof, palg = run_workload(extra_cfg, layers["prefill"], args.seed, max(10, args.steps // 10),
+                                        max(5, args.warmup // 4), args.path, graph=args.graph)
         pk = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in pprof.items()}
         out["prefill"] = dict(workload=extra_cfg["name"], ms_per_step=pms,
                               tokens_s=extra_cfg["T"] / (pms * 1e-3), alg_flops=palg["flops"],
                               tflops=palg["flops"] / (pms * 1e-3) / 1e12,
                               mfma_frac=palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                              expert_counts=palg["counts"], kernels=pk)
+                              expert_counts=palg["counts"], step_ms_dist=palg["step_ms_dist"], kernels=pk)
     del layers
     if args.workload == "decode" and not args.no_extra and not args.no_others:
         # the other three layers of the workload set, measured the same way
