@@ -31,6 +31,18 @@
 namespace moeq {
 
 constexpr int kXStride = 4 * kTileK + 8;   // halves per staged activation row
+
+// Staging buffers per class: the 16-token INT class (occupancy 4 by
+// registers) has LDS to spare for two, which saves one barrier per tile
+// group; the larger classes and the bit-plane kernels (per-wave LUTs in
+// LDS) keep one.  Sizes of one buffer: activations (halves) and per-group
+// column sums (floats, 4 tiles x up to 2 groups x rows).
+template <int NSUB, bool PLANE>
+__host__ __device__ constexpr int xs_bufs() { return NSUB == 1 && !PLANE ? 2 : 1; }
+template <int NSUB>
+__host__ __device__ constexpr int xs_halves() { return NSUB * 16 * kXStride; }
+template <int NSUB>
+__host__ __device__ constexpr int sx_floats() { return 8 * NSUB * 16; }
 constexpr int kLutBlk = 4 * 16 * 16;       // halves of one block's staged LUTs (4 tiles x 16 rows x 16)
 
 // Packed data of one strip of one block for one group of C tiles.
@@ -408,23 +420,32 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
   const int n_kt = d0.K / kTileK;
   const int full = n_kt / 4;                   // groups with 4 tiles
   const int g_full_end = std::min(g_end, full);
+  // staging buffers of group g (two alternate when the LDS allows: then
+  // one barrier per group suffices, see group_step)
+  constexpr int NXB = xs_bufs<NSUB, PLANE>();
+  auto xb = [&](int g) { return xs + (NXB == 2 ? (g & 1) * xs_halves<NSUB>() : 0); };
+  auto sb = [&](int g) { return sx + (NXB == 2 ? (g & 1) * sx_floats<NSUB>() : 0); };
   Stager<NSUB, NW, PLANE, B0, B1, GPT> stg;
   {
     const int c = std::min(4, n_kt - 4 * g_begin);
     stg.load(d0, d1, rowp, s0, s1, g_begin, n_kt, c);
-    stg.store(xs, sx, lut_lds, c);
+    stg.store(xb(g_begin), sb(g_begin), lut_lds, c);
     __syncthreads();
   }
   // one full group: the next group's activations load, this group is
-  // decoded and multiplied, then the activations are published
+  // decoded and multiplied, then the activations are published.  With one
+  // buffer the store waits for every wave to finish reading it; with two it
+  // goes to the buffer that the barrier of the previous group already
+  // freed, and the one barrier after it publishes it.  (Bit-plane LUTs are
+  // per wave: a wave overwrites only rows it has finished reading.)
   auto group_step = [&](int g, const Group<B0, PLANE> &c0, const Group<B1, PLANE> &c1) {
     const bool more = g + 1 < g_end;
     const int cn = more ? std::min(4, n_kt - 4 * (g + 1)) : 0;
     if (more) stg.load(d0, d1, rowp, s0, s1, g + 1, n_kt, cn);
-    compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xs, sx, lut_lds, acc);
+    compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xb(g), sb(g), lut_lds, acc);
     if (more) {
-      __syncthreads();
-      stg.store(xs, sx, lut_lds, cn);
+      if constexpr (NXB == 1) __syncthreads();
+      stg.store(xb(g + 1), sb(g + 1), lut_lds, cn);
       __syncthreads();
     }
   };
@@ -445,13 +466,13 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
     switch (n_kt - 4 * full) {
       case 1:
         load_group<B0, PLANE, 1, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 1, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 1, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 1, GPT>(t0, t1, xb(full), sb(full), lut_lds, acc); break;
       case 2:
         load_group<B0, PLANE, 2, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 2, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 2, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 2, GPT>(t0, t1, xb(full), sb(full), lut_lds, acc); break;
       default:
         load_group<B0, PLANE, 3, GPT>(d0, s0, full, n_kt, t0); load_group<B1, PLANE, 3, GPT>(d1, s1, full, n_kt, t1);
-        compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xs, sx, lut_lds, acc); break;
+        compute_two<NSUB, B0, B1, PLANE, 3, GPT>(t0, t1, xb(full), sb(full), lut_lds, acc); break;
     }
   }
   if constexpr (!PLANE) {                      // INT sums are in units of 2^-24
@@ -494,17 +515,18 @@ __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a
 // LDS layout of both stream kernels: [x staging | z rows (2 RZ columns) |
 // per-group column sums (4 tiles x 2 groups x NSUB*16 rows, fp32) | per wave:
 // its two streams' bit-plane LUTs].
-template <int NSUB>
-__device__ __forceinline__ int zs_offset() { return NSUB * 16 * kXStride; }
+template <int NSUB, bool PLANE>
+__device__ __forceinline__ int zs_offset() { return xs_bufs<NSUB, PLANE>() * xs_halves<NSUB>(); }
 
-template <int NSUB>
+template <int NSUB, bool PLANE>
 __device__ __forceinline__ float *sx_region(uint16_t *lds, int RZ) {
-  return reinterpret_cast<float *>(lds + NSUB * 16 * kXStride + NSUB * 16 * 2 * RZ);
+  return reinterpret_cast<float *>(lds + zs_offset<NSUB, PLANE>() + NSUB * 16 * 2 * RZ);
 }
 
-template <int NSUB>
+template <int NSUB, bool PLANE>
 __device__ __forceinline__ uint16_t *lut_region(uint16_t *lds, int RZ, int wave) {
-  return reinterpret_cast<uint16_t *>(sx_region<NSUB>(lds, RZ) + 8 * NSUB * 16) + wave * 2 * kLutBlk;
+  return reinterpret_cast<uint16_t *>(sx_region<NSUB, PLANE>(lds, RZ) +
+                                     xs_bufs<NSUB, PLANE>() * sx_floats<NSUB>()) + wave * 2 * kLutBlk;
 }
 
 // gate/up: 4 waves, each streams the gate and the up rows of one 16-row
@@ -514,7 +536,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t *xs = lds;
-  uint16_t *zs = lds + zs_offset<NSUB>();
+  uint16_t *zs = lds + zs_offset<NSUB, PLANE>();
   const int zw = 2 * a.RZ;
   const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];   // scalar loads
   Group<BG, PLANE> p0;
@@ -532,8 +554,8 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.H / kTileK + 3) / 4;
-  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, sx_region<NSUB>(lds, a.RZ),
-                                          lut_region<NSUB>(lds, a.RZ, wave), acc, p0, p1);
+  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
+                                          lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
   const int row = strip * 16 + (lane & 15);
   if (a.comp_on) {
 #pragma unroll
@@ -564,7 +586,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t *xs = lds;
-  uint16_t *zs = lds + zs_offset<NSUB>();
+  uint16_t *zs = lds + zs_offset<NSUB, PLANE>();
   const int zw = a.RZ;
   const bool epi = a.comp_on && split == 0;
   const BlockDesc d = a.desc[3 * ch.e + 2];                          // scalar loads
@@ -586,8 +608,8 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (g1 > g0)
-    stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, sx_region<NSUB>(lds, a.RZ),
-                                            lut_region<NSUB>(lds, a.RZ, wave), acc, p0, p1);
+    stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
+                                            lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -623,7 +645,8 @@ __device__ __forceinline__ int class_of(int cnt, int nsub_max) {
 
 // LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
 inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
-  return (size_t)nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 2 * RZ * 2 + (size_t)8 * nsub * 16 * 4 +
+  const size_t nb = plane ? 1 : (nsub == 1 ? xs_bufs<1, false>() : 1);
+  return nb * nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 2 * RZ * 2 + nb * 8 * nsub * 16 * 4 +
          (plane ? (size_t)4 * 2 * kLutBlk * 2 : 0);
 }
 
