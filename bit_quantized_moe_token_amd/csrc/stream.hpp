@@ -355,20 +355,34 @@ __device__ __forceinline__ void z_prologue(const float *zpart, int zstride, int6
   }
 }
 
+// B operand of U for z columns 32 ks .. 32 ks + 31 of output row `row`
+// (zero past the rank R).
+__device__ __forceinline__ f16x8 lowrank_bop(const uint16_t *U, int R, int row, int ks) {
+  const int col = 32 * ks + 8 * ((threadIdx.x & 63) >> 4);
+  return col < R ? load_a(U + (int64_t)row * R + col) : pack_b(0, 0, 0, 0);
+}
+
 // Low-rank epilogue: acc += U z for one factor set (z rows in LDS, zero for
-// uncompensated pairs and for columns >= R).
+// uncompensated pairs and for columns >= R).  b0: the operand of the first
+// 32 columns, loaded by the caller (the streaming kernels load it before
+// their K walk, so the epilogue does not wait for it).
 template <int NSUB>
 __device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, int row, const uint16_t *zs,
-                                            int zwidth, f32x4 *acc) {
+                                            int zwidth, f32x4 *acc, f16x8 b0) {
   const int lane = threadIdx.x & 63, kq = lane >> 4;
   for (int ks = 0; ks < Rpad / 32; ++ks) {
     const int col = 32 * ks + 8 * kq;
-    f16x8 bop = pack_b(0, 0, 0, 0);
-    if (col < R) bop = load_a(U + (int64_t)row * R + col);
+    const f16x8 bop = ks == 0 ? b0 : lowrank_bop(U, R, row, ks);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
       acc[s] = mfma16(*reinterpret_cast<const f16x8 *>(zs + (16 * s + (lane & 15)) * zwidth + col), bop, acc[s]);
   }
+}
+
+template <int NSUB>
+__device__ __forceinline__ void lowrank_epi(const uint16_t *U, int R, int Rpad, int row, const uint16_t *zs,
+                                            int zwidth, f32x4 *acc) {
+  lowrank_epi<NSUB>(U, R, Rpad, row, zs, zwidth, acc, lowrank_bop(U, R, row, 0));
 }
 
 // Stage group g's activations (and the two streams' bit-plane LUTs) into
@@ -548,6 +562,15 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, true);
+  const int row = strip * 16 + (lane & 15);
+  // first U operands (gate, up), requested before the K walk where the
+  // registers allow (not in the 64-token class)
+  constexpr bool kPreU = NSUB <= 2;
+  f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
+  if (kPreU && a.comp_on && a.r > 0) {
+    ub[0] = lowrank_bop(dg.U, a.r, row, 0);
+    ub[1] = lowrank_bop(du.U, a.r, row, 0);
+  }
   f32x4 acc[2][NSUB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -556,12 +579,14 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   const int n_g4 = (a.H / kTileK + 3) / 4;
   stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
                                           lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
-  const int row = strip * 16 + (lane & 15);
   if (a.comp_on) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const BlockDesc &d = b ? du : dg;
-      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b]);
+      if (a.r > 0) {
+        if (kPreU) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b], ub[b]);
+        else lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b]);
+      }
       if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[b]);
     }
   }
@@ -602,6 +627,14 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, false);
+  // first U operands of the two strips, requested before the K walk where
+  // the registers allow (not in the 64-token class)
+  constexpr bool kPreU = NSUB <= 2;
+  f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
+  if (kPreU && epi && a.r > 0) {
+    ub[0] = lowrank_bop(d.U, a.r, st0 * 16 + (lane & 15), 0);
+    ub[1] = lowrank_bop(d.U, a.r, st1 * 16 + (lane & 15), 0);
+  }
   f32x4 acc[2][NSUB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -615,7 +648,10 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   for (int b = 0; b < 2; ++b) {
     const int row = (b ? st1 : st0) * 16 + (lane & 15);
     if (epi) {
-      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b]);
+      if (a.r > 0) {
+        if (kPreU) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b], ub[b]);
+        else lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b]);
+      }
       if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + a.Rp, zw, acc[b]);
     }
 #pragma unroll
