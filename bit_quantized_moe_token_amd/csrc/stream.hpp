@@ -362,6 +362,45 @@ __device__ __forceinline__ f16x8 lowrank_bop(const uint16_t *U, int R, int row, 
   return col < R ? load_a(U + (int64_t)row * R + col) : pack_b(0, 0, 0, 0);
 }
 
+// z rows of a chunk held in registers from before the K walk until the
+// epilogue (one fp32 partial, width <= 8 * NW * 64 * 4 / (NSUB * 16)): the
+// same values z_prologue would load, without its wait at the end.
+template <int NSUB, int NW, int NV>
+struct ZPre {
+  f32x4 v[NV];
+};
+
+template <int NSUB, int NW, int NV>
+__device__ __forceinline__ void z_preload(const float *zpart, int zstride, int width, const Chunk &ch,
+                                          ZPre<NSUB, NW, NV> &zp) {
+  const int tid = threadIdx.x;
+  const int n4 = NSUB * 16 * width / 4;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int o = tid + i * NW * 64;
+    const int row = (4 * o) / width, col = (4 * o) % width;
+    const int m = std::min(row, ch.cnt - 1);
+    zp.v[i] = o < n4 ? gld<f32x4>(zpart + (int64_t)(ch.base + m) * zstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <int NSUB, int NW, int NV>
+__device__ __forceinline__ void z_store(const ZPre<NSUB, NW, NV> &zp, int width, uint16_t *zs) {
+  const int tid = threadIdx.x;
+  const int n4 = NSUB * 16 * width / 4;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int o = tid + i * NW * 64;
+    if (o < n4) {
+      const int row = (4 * o) / width, col = (4 * o) % width;
+      u32x2 h;
+      h[0] = as_u32(f16x2{(f16)zp.v[i][0], (f16)zp.v[i][1]});
+      h[1] = as_u32(f16x2{(f16)zp.v[i][2], (f16)zp.v[i][3]});
+      *reinterpret_cast<u32x2 *>(zs + row * width + col) = h;
+    }
+  }
+}
+
 // Low-rank epilogue: acc += U z for one factor set (z rows in LDS, zero for
 // uncompensated pairs and for columns >= R).  b0: the operand of the first
 // 32 columns, loaded by the caller (the streaming kernels load it before

@@ -273,19 +273,31 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
                                make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * 2u),
                                make_rsrc(dg.codes, code_region_bytes(dg)),
                                make_rsrc(du.codes, code_region_bytes(du))};
+  // the low-rank epilogue's inputs (z rows for up to 64 columns from one
+  // partial, and the first U operands) are requested before the K walk, so
+  // the epilogue does not wait for memory
+  const int zw = 2 * a.RZ;
+  const bool zpre = a.comp_on && a.ks_gu == 1 && zw <= 64;
+  ZPre<8, 4, 8> zp;
+  if (zpre) z_preload<8, 4, 8>(a.zp_gu, zw, zw, ch, zp);
+  f16x8 ub[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    ub[q] = a.comp_on && a.r > 0 ? lowrank_bop((q >> 1) ? du.U : dg.U, a.r, strips[q] * 16 + (lane & 15), 0)
+                                 : pack_b(0, 0, 0, 0);
   kl.template run<8>(acc);
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
     uint16_t *zs = l16;
-    const int zw = 2 * a.RZ;
-    z_prologue<8, 4>(a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    if (zpre) z_store<8, 4, 8>(zp, zw, zs);
+    else z_prologue<8, 4>(a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int b = q >> 1;
       const BlockDesc &d = b ? du : dg;
       const int row = strips[q] * 16 + (lane & 15);
-      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[q]);
+      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[q], ub[q]);
       if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[q]);
     }
     __syncthreads();
