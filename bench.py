@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
+    p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
+                   help="reduce a kernel trace and an SQ counter pass (MFMA, VALU) of the workload's command "
+                        "to profiles/counters_<workload>.md")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, "
                         "WRITE_SIZE) of a --copy-calibration run and record the scaled "
@@ -321,6 +324,92 @@ def _read_pmc(folder, counter):
     return vals
 
 
+SQ_KEYS = [("tiled_gateup", "gateup_tiled"), ("tiled_down", "down_tiled"), ("gateup_kernel", "gateup_stream"),
+           ("down_kernel", "down_stream"), ("lowrank", "lowrank_project"), ("route", "route"), ("combine", "combine")]
+SQ_COUNTERS = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_WAVES", "SQ_BUSY_CYCLES",
+               "GRBM_GUI_ACTIVE"]
+MFMA_FLOPS = 16 * 16 * 32 * 2      # every MFMA of these kernels is v_mfma_f32_16x16x32_f16
+N_SIMD = 256 * 4
+N_XCD = 8                           # GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs
+
+
+def _sq_key(name):
+    return next((k for pat, k in SQ_KEYS if pat in name), None)
+
+
+def summarize_sq(workload, trace_dir, sq_dir):
+    """MFMA and VALU counters per kernel from one rocprofv3 --pmc pass
+    (SQ_COUNTERS) and the kernel trace of the same command: MFMA
+    instructions x 16384 flops over the mean duration (counter TFLOP/s), the
+    MFMA-busy share of SIMD cycles, the clock the GPU-active cycle count
+    implies.  Writes profiles/counters_<workload>.md."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    dur = {}
+    for row in csv.DictReader(open(stats[0])):
+        key = _sq_key(row["Name"])
+        if key:
+            c, t = dur.get(key, (0, 0.0))
+            dur[key] = (c + int(row["Calls"]), t + float(row["TotalDurationNs"]))
+    per = {}
+    for fn in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(fn)):
+            key = _sq_key(row.get("Kernel_Name", ""))
+            if key is None or row.get("Counter_Name") not in SQ_COUNTERS:
+                continue
+            d = (fn, row["Dispatch_Id"], key, row["Counter_Name"])
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+    vals = {}
+    for (_, _, key, cn), v in per.items():
+        vals.setdefault(key, {}).setdefault(cn, []).append(v)
+    lines = [f"# MFMA and VALU counters per kernel, {workload}", "",
+             "Two runs of the same command (a kernel trace, then one counter pass with "
+             f"{' '.join(SQ_COUNTERS)}) and their reduction:", "", "```",
+             f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o kt --output-format csv -- "
+             f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+             f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {sq_dir} -o pmc --output-format csv -- "
+             f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+             f"python3 bench.py --workload {workload_short(workload)} --summarize-sq {trace_dir} {sq_dir}", "```", "",
+             "Per dispatch (means). MFMA TFLOP/s = SQ_INSTS_MFMA x 16384 / mean duration (every MFMA here is "
+             "16x16x32 fp16; padding rows and the low-rank MFMAs count). GRBM_GUI_ACTIVE sums the 8 XCDs' "
+             "active cycles, so the clock = GRBM_GUI_ACTIVE / 8 / mean duration, and MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs): the share of the MFMA peak at "
+             "that clock (it agrees with MFMA TFLOP/s over the peak scaled to the clock). Clock and busy "
+             "figures of kernels of a few microseconds are dominated by launch and drain.", "",
+             "| kernel | dispatches | mean us | MFMA instr | MFMA TFLOP/s | of 2.5 PF | MFMA busy | VALU instr | "
+             "waves | clock GHz |", "|---|---|---|---|---|---|---|---|---|---|"]
+    stat = statistics.mean
+    for key in [k for _, k in SQ_KEYS]:
+        if key not in vals or key not in dur:
+            continue
+        v = {cn: stat(x) for cn, x in vals[key].items()}
+        us = dur[key][1] / dur[key][0] / 1e3
+        mf = v.get("SQ_INSTS_MFMA", 0.0)
+        tf = mf * MFMA_FLOPS / (us * 1e-6) / 1e12
+        act = v.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (act * N_SIMD) if act else float("nan")
+        clk = act / (us * 1e-6) / 1e9 if act else float("nan")
+        lines.append(f"| {key} | {len(vals[key].get('SQ_INSTS_MFMA', []))} | {us:.1f} | {mf:.4g} | {tf:.1f} | "
+                     f"{tf / MFMA_F16_PEAK_TFLOPS:.3f} | {busy:.3f} | {v.get('SQ_INSTS_VALU', 0.0):.4g} | "
+                     f"{v.get('SQ_WAVES', 0.0):.4g} | {clk:.2f} |")
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", f"counters_{workload_short(workload)}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def workload_short(name):
+    from synth import configs
+    for short in ("decode", "prefill", "finegrained", "bitplane", "tiny"):
+        if configs.get(short)["name"] == name:
+            return short
+    return name
+
+
 def summarize_pmc(workload, fetch_dir, write_dir):
     fe = _read_pmc(fetch_dir, "FETCH_SIZE")
     wr = _read_pmc(write_dir, "WRITE_SIZE")
@@ -388,6 +477,10 @@ def cpu_baseline(cfg, seed, sample_tokens, min_seconds=12.0):
 
 def main():
     args = parse()
+    if args.summarize_sq:
+        from synth import configs
+        summarize_sq(configs.get(args.workload)["name"], *args.summarize_sq)
+        return
     if args.summarize_pmc:
         from synth import configs
         summarize_pmc(configs.get(args.workload)["name"], *args.summarize_pmc)
