@@ -50,6 +50,9 @@ SIGNATURES = [
     ("moeq_abi_version", c_i32, []),
     ("moeq_quantize_rtn", c_i32, [c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_void_p]),
     ("moeq_build_lut", c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p, c_void_p]),
+    ("moeq_fit_lowrank_workspace_size", c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
+    ("moeq_fit_lowrank", c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p,
+                                 c_i32, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     ("moeq_pack_size", c_i32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(c_size_t)]),
     ("moeq_pack", c_i32, [ctypes.POINTER(LayerDesc), c_void_p, c_size_t, c_void_p, ctypes.POINTER(c_void_p)]),
     ("moeq_layer_destroy", None, [c_void_p]),

@@ -64,6 +64,29 @@ def build_lut(w, codes4, scales, zeros, q, G):
     return lut
 
 
+def fit_lowrank(w, codes, scales, zeros, G, omega, r, power_iters=2):
+    """Rank-r compensator factors (U fp16 [N, r], V fp16 [r, K]) of the mean
+    RTN residual of the blocks w [n, N, K] (or one block [N, K]); omega
+    fp32 [K, l] is the Gaussian test matrix (see moeq_fit_lowrank)."""
+    if w.dim() == 2:
+        w, codes, scales, zeros = (t.unsqueeze(0) for t in (w, codes, scales, zeros))
+    n_mat, N, K = w.shape
+    l = omega.shape[1]
+    _need(w, torch.float16, (n_mat, N, K), "w")
+    _need(codes, torch.uint8, (n_mat, N, K), "codes")
+    _need(scales, torch.float16, (n_mat, N, K // G), "scales")
+    _need(zeros, torch.uint8, (n_mat, N, K // G), "zeros")
+    _need(omega, torch.float32, (K, l), "omega")
+    n = ctypes.c_size_t(0)
+    check(lib().moeq_fit_lowrank_workspace_size(N, K, r, l, ctypes.byref(n)), "moeq_fit_lowrank_workspace_size")
+    ws = torch.empty((max(1, n.value),), dtype=torch.uint8, device=w.device)
+    U = torch.empty((N, r), dtype=torch.float16, device=w.device)
+    V = torch.empty((r, K), dtype=torch.float16, device=w.device)
+    check(lib().moeq_fit_lowrank(_ptr(w), _ptr(codes), _ptr(scales), _ptr(zeros), n_mat, N, K, G, _ptr(omega), l, r,
+                                 power_iters, _ptr(U), _ptr(V), _ptr(ws), n.value, _stream()), "moeq_fit_lowrank")
+    return U, V
+
+
 # ---------------------------------------------------------------- layer
 
 def _ptr_array(tensors):

@@ -117,6 +117,34 @@ moeq_status moeq_build_lut(const uint16_t *w, const uint8_t *codes4,
                            int32_t K, int32_t G, int32_t q, uint16_t *lut,
                            hipStream_t stream);
 
+/*
+ * moeq_fit_lowrank — rank-r compensator factors of the quantization residual
+ * (data preparation, before the path; [MiLo] abstract: low-rank
+ * compensators of the quantized experts; [TileQ] abstract: factors shared
+ * by a group of experts).  The residual is the mean over n_mat blocks
+ *   R = (1/n_mat) sum_m (w_m - s_m * (c_m - z_m))
+ * (n_mat = 1: one block's compensator; n_mat > 1: the pair shared by a
+ * group, which minimizes sum_m ||R_m - U V||_F).  U V approximates the
+ * rank-r truncation of R by randomized subspace iteration (Halko,
+ * Martinsson and Tropp): Y = R omega, power_iters steps of Y = R orth(R^T
+ * orth(Y)), Q = orth(Y), then the exact SVD of Q^T R; the singular values
+ * are split evenly: U = P sqrt(S), V = sqrt(S) Q'^T.
+ *   w DEVICE [n_mat, N, K] fp16; codes DEVICE [n_mat, N, K] uint8;
+ *   scales DEVICE [n_mat, N, K/G] fp16; zeros DEVICE [n_mat, N, K/G] uint8
+ *   (the RTN outputs of moeq_quantize_rtn for each block);
+ *   omega DEVICE [K, l] fp32, drawn by the caller (e.g. N(0, 1));
+ *   1 <= r <= l <= min(N, K, 128); power_iters in 0..16;
+ *   U DEVICE [N, r] fp16 out; V DEVICE [r, K] fp16 out;
+ *   ws DEVICE, at least moeq_fit_lowrank_workspace_size bytes.
+ * The l x l factorizations run on the host in fp64: the call synchronizes
+ * the stream (offline preparation, not part of the hot path).
+ */
+moeq_status moeq_fit_lowrank_workspace_size(int32_t N, int32_t K, int32_t r, int32_t l, size_t *bytes);
+moeq_status moeq_fit_lowrank(const uint16_t *w, const uint8_t *codes, const uint16_t *scales,
+                             const uint8_t *zeros, int32_t n_mat, int32_t N, int32_t K, int32_t G,
+                             const float *omega, int32_t l, int32_t r, int32_t power_iters, uint16_t *U,
+                             uint16_t *V, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* -------------------------------------------------------- packed layer -- */
 
 typedef struct moeq_layer moeq_layer; /* opaque host handle */

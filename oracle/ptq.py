@@ -89,6 +89,19 @@ def bitplane_lut(W16, c4, s16, z, q, G):
     return lut
 
 
+def mean_residual_compensator(W16_list, W_hat_list, r):
+    """Rank-r factor pair shared by n blocks (TileQ abstract: factors shared
+    across experts): the truncated SVD of the mean residual
+    R = (1/n) sum_m (W_m - W_hat_m).  It minimizes sum_m ||R_m - U V||_F^2
+    over rank-r U V, since sum_m ||R_m - X||^2 = sum_m ||R_m - R||^2 +
+    n ||R - X||^2.  Same return values and split as svd_compensator; n = 1
+    is svd_compensator itself.
+    """
+    Rm = [np.asarray(W, dtype=np.float64) - np.asarray(Wh, dtype=np.float64) for W, Wh in zip(W16_list, W_hat_list)]
+    mean = sum(Rm) / len(Rm)
+    return svd_compensator(mean, np.zeros_like(mean), r)
+
+
 def svd_compensator(W16, W_hat, r):
     """Rank-r compensator of the quantization residual R = W - W_hat.
 

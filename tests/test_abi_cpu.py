@@ -133,3 +133,17 @@ def test_ffn_validation(L):
     n = ctypes.c_size_t(0)
     assert L.moeq_ffn_workspace_size(None, 4, 2, None, ctypes.byref(n)) == 1
     assert L.moeq_debug_unpack(None, 0, 0, None, None) == 1
+
+
+def test_fit_lowrank_validation_cpu(L):
+    # argument errors are reported before any device work
+    n = ctypes.c_size_t(0)
+    assert L.moeq_fit_lowrank_workspace_size(512, 256, 8, 16, ctypes.byref(n)) == 0 and n.value > 512 * 256 * 4
+    assert L.moeq_fit_lowrank_workspace_size(512, 256, 8, 4, ctypes.byref(n)) == 1      # l < r
+    assert L.moeq_fit_lowrank_workspace_size(512, 256, 8, 129, ctypes.byref(n)) == 1    # l > 128
+    p = ctypes.c_void_p(16)
+    assert L.moeq_fit_lowrank(None, p, p, p, 1, 512, 256, 64, p, 16, 8, 2, p, p, p, 1 << 30, None) == 1
+    assert L.moeq_fit_lowrank(p, p, p, p, 1, 512, 256, 60, p, 16, 8, 2, p, p, p, 1 << 30, None) == 1   # G !| K
+    assert L.moeq_fit_lowrank(p, p, p, p, 0, 512, 256, 64, p, 16, 8, 2, p, p, p, 1 << 30, None) == 1   # n_mat
+    assert L.moeq_fit_lowrank(p, p, p, p, 1, 512, 256, 64, p, 16, 8, 17, p, p, p, 1 << 30, None) == 1  # iters
+    assert L.moeq_fit_lowrank(p, p, p, p, 1, 512, 256, 64, p, 16, 8, 2, p, p, p, 16, None) == 3        # workspace

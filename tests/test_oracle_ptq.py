@@ -170,3 +170,36 @@ def test_svd_compensator_eckart_young():
     # the balanced split puts the same singular values on both sides
     U16, V16, U64, V64, S = ptq.svd_compensator(W, W_hat, 8)
     assert np.allclose(np.linalg.norm(U64, axis=0), np.linalg.norm(V64, axis=1))
+
+
+def test_mean_residual_compensator_minimizes_the_group_objective():
+    """The shared pair of n residuals: the identity sum ||R_m - X||^2 =
+    sum ||R_m - mean||^2 + n ||mean - X||^2 holds for it, no rank-r
+    competitor (least-squares fits to random column spaces, and each
+    block's own truncated SVD) gives a smaller group objective, and n = 1
+    reduces to svd_compensator."""
+    rng = np.random.default_rng(3)
+    N, K, r, n = 96, 80, 6, 3
+    common = rng.standard_normal((N, r)) @ rng.standard_normal((r, K)) * 0.01
+    Ws = [(common + rng.standard_normal((N, K)) * 0.004).astype(np.float16) for _ in range(n)]
+    Whs = [np.zeros((N, K)) for _ in range(n)]
+    U16, V16, U64, V64, S = ptq.mean_residual_compensator(Ws, Whs, r)
+    Rm = [W.astype(np.float64) for W in Ws]
+    mean = sum(Rm) / n
+    X = U64 @ V64
+    obj = sum(np.sum((R - X) ** 2) for R in Rm)
+    assert obj == pytest.approx(sum(np.sum((R - mean) ** 2) for R in Rm) + n * np.sum((mean - X) ** 2), rel=1e-12)
+    assert np.linalg.matrix_rank(X) == r
+    competitors = []
+    for _ in range(4):
+        A = rng.standard_normal((N, r))
+        competitors.append(A @ np.linalg.lstsq(A, mean, rcond=None)[0])
+    for R in Rm:
+        _, _, Ua, Va, _ = ptq.svd_compensator(R, np.zeros_like(R), r)
+        competitors.append(Ua @ Va)
+    for C in competitors:
+        assert sum(np.sum((R - C) ** 2) for R in Rm) >= obj * (1 - 1e-12)
+    # one block: the same factors as svd_compensator
+    _, _, U1, V1, _ = ptq.mean_residual_compensator(Ws[:1], Whs[:1], r)
+    _, _, U2, V2, _ = ptq.svd_compensator(Ws[0], Whs[0], r)
+    assert np.allclose(U1 @ V1, U2 @ V2, rtol=0, atol=1e-15)
