@@ -20,6 +20,10 @@ CASES = {
     "prefill": ("prefill", dict(H=512, I=1792, T=1024)),
     "finegrained": ("finegrained", {}),
     "bitplane": ("bitplane", dict(E=32, T=128)),
+    # the largest expert count (256): experts with one or two pairs, chunk
+    # lookup over four 64-lane passes, routing with E = 256
+    "many_experts": ("finegrained", dict(E=256, k=8, T=48, H=256, I=256)),
+    "many_experts_bitplane": ("bitplane", dict(E=256, T=40, H=256, I=256)),
 }
 
 _cache = {}
