@@ -25,7 +25,11 @@
 //     c 2^(p - 24).  Multiplied by activations pre-scaled by 2^-p per column
 //     it gives c x 2^-24 exactly inside the MFMA (streaming kernels).
 // Bit-plane packing (4 bytes per plane per lane per tile): the bit of code
-// plane c for the weight (pair P = 4j + v, half h) is at bit 16h + 4v + j.
+// plane c for register element i = 2v + h of step j (pair P = 4j + v, half
+// h) is at bit 8 (i mod 4) + 4 (i div 4) + j.  The four weights of a quad
+// (elements 4qd .. 4qd + 3 of a step) thus sit at the same bit s = 4qd + j
+// of the four bytes, so one shift and one mask per plane spread a quad's
+// indices one per byte: the byte selectors of v_perm.
 #pragma once
 #include "common.hpp"
 
@@ -197,33 +201,61 @@ __device__ __forceinline__ f16x8 rescale_a(f16x8 a) {
   }
 }
 
-// Merged q-bit indices of MFMA step j from the top q planes (pl[0] = plane
-// 3): nibble v of the low half is the index of the low weight of pair v,
-// nibble v of the high half that of the high weight.
+// Bit of element i (0..7) of step j in a plane dword.
+__host__ __device__ constexpr int plane_bit(int j, int i) { return 8 * (i % 4) + 4 * (i / 4) + j; }
+
+// x >> d for d >= 0, x << -d otherwise (d folds to a constant once the
+// step loops are unrolled).
+__device__ __forceinline__ uint32_t shift_r(uint32_t x, int d) { return d >= 0 ? x >> d : x << -d; }
+
+// The low min(q, 3) bits of the q-bit indices of a quad, weight e in byte
+// e, from the top q planes (pl[0] = plane 3, the index's most significant
+// bit); s = 4 qd + j.
 template <int Q>
-__device__ __forceinline__ uint32_t plane_merge(const uint32_t *pl, int j) {
-  uint32_t m = 0;
+__device__ __forceinline__ uint32_t plane_sel(const uint32_t *pl, int s) {
+  uint32_t sel = 0;
 #pragma unroll
-  for (int u = 0; u < Q; ++u) m |= ((pl[u] >> j) & 0x11111111u) << (Q - 1 - u);
-  return m;
+  for (int u = Q > 3 ? 1 : 0; u < Q; ++u) {
+    const int b = Q - 1 - u;
+    sel |= shift_r(pl[u], s - b) & (0x01010101u << b);
+  }
+  return sel;
 }
 
-// LUT lookup of a pair of q-bit indices w = i_lo | i_hi << 16 in the lane's
-// row table L (2^q fp16 entries in 2^(q-1) dwords).
+// q = 4: selector that takes byte e from the entries-8..15 lookup when
+// index bit 3 of weight e is set, else from the entries-0..7 lookup.
+__device__ __forceinline__ uint32_t plane_top(const uint32_t *pl, int s) {
+  return (shift_r(pl[0], s - 2) & 0x04040404u) | 0x03020100u;
+}
+
+// Full q-bit index of weight e of a quad (debug read-back).
 template <int Q>
-__device__ __forceinline__ uint32_t lut_pair(uint32_t w, const uint32_t *L) {
-  const uint32_t sel = (w & 0x00030003u) * 0x0202u + 0x01000100u;
-  if (Q == 2) return __builtin_amdgcn_perm(L[1], L[0], sel);
-  const uint32_t r0 = __builtin_amdgcn_perm(L[1], L[0], sel);
-  const uint32_t r1 = __builtin_amdgcn_perm(L[3], L[2], sel);
-  const uint32_t m2 = ((w >> 2) & 0x00010001u) * 0xFFFFu;
-  const uint32_t a = (m2 & r1) | (~m2 & r0);
-  if (Q == 3) return a;
-  const uint32_t r2 = __builtin_amdgcn_perm(L[5], L[4], sel);
-  const uint32_t r3 = __builtin_amdgcn_perm(L[7], L[6], sel);
-  const uint32_t b = (m2 & r3) | (~m2 & r2);
-  const uint32_t m3 = ((w >> 3) & 0x00010001u) * 0xFFFFu;
-  return (m3 & b) | (~m3 & a);
+__device__ __forceinline__ uint32_t plane_index(const uint32_t *pl, int s, int e) {
+  const uint32_t lo = (plane_sel<Q>(pl, s) >> (8 * e)) & 7u;
+  if constexpr (Q < 4) return lo;
+  else return lo | (((plane_top(pl, s) >> (8 * e + 2)) & 1u) << 3);
+}
+
+// One byte (low or high) of the LUT entries of a quad's four weights from
+// that byte's table T (2^q bytes in 2^q / 4 dwords, entry i in byte i).
+template <int Q>
+__device__ __forceinline__ uint32_t quad_bytes(const uint32_t *T, uint32_t sel, uint32_t top) {
+  if constexpr (Q == 2) return __builtin_amdgcn_perm(T[0], T[0], sel);
+  else if constexpr (Q == 3) return __builtin_amdgcn_perm(T[1], T[0], sel);
+  else return __builtin_amdgcn_perm(__builtin_amdgcn_perm(T[3], T[2], sel), __builtin_amdgcn_perm(T[1], T[0], sel), top);
+}
+
+// The quad's four fp16 weights as two dwords (elements 4qd, 4qd+1 and
+// 4qd+2, 4qd+3) from the lane's row table L: the low bytes of the 2^q
+// entries in 2^q / 4 dwords, then their high bytes.
+template <int Q>
+__device__ __forceinline__ void plane_quad(const uint32_t *pl, int s, const uint32_t *L, uint32_t &d0, uint32_t &d1) {
+  const uint32_t sel = plane_sel<Q>(pl, s);
+  const uint32_t top = Q == 4 ? plane_top(pl, s) : 0u;
+  const uint32_t lo = quad_bytes<Q>(L, sel, top);
+  const uint32_t hi = quad_bytes<Q>(L + (1 << Q) / 4, sel, top);
+  d0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 }  // namespace moeq

@@ -70,7 +70,7 @@ pack_planes_kernel(const uint8_t *__restrict__ codes, int N, int K, uint8_t *__r
     for (int h = 0; h < 2; ++h) {
       const uint32_t c = src[tile_col(t, l, P, h)] & 15u;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) pl[b] |= ((c >> b) & 1u) << (16 * h + 4 * v + j);
+      for (int b = 0; b < 4; ++b) pl[b] |= ((c >> b) & 1u) << plane_bit(j, 2 * v + h);
     }
   }
   const uint64_t off = code_offset(s, t, l, n_kt, 4);
@@ -105,7 +105,7 @@ pack_lut_kernel(const uint16_t *__restrict__ lut, int N, int K, int q, uint16_t 
 }
 
 // Debug read-back: one thread per (strip, tile, lane), same decode as the
-// expert kernels.  INT: (c - 0) pairs; bit-plane: merged q-bit indices.
+// expert kernels.  INT: (c - 0) pairs; bit-plane: the q-bit indices.
 template <int B>
 __global__ void __launch_bounds__(256)
 unpack_int_kernel(const uint8_t *__restrict__ packed, int N, int K, uint8_t *__restrict__ out) {
@@ -146,13 +146,9 @@ unpack_planes_kernel(const uint8_t *__restrict__ packed, uint64_t plane_bytes, i
   uint8_t *dst = out + (int64_t)(s * kStripRows + (l & 15)) * K;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t m = plane_merge<Q>(pl, j);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t w = (m >> (4 * v)) & 0x000F000Fu;
-      dst[tile_col(t, l, 4 * j + v, 0)] = (uint8_t)(w & 0xF);
-      dst[tile_col(t, l, 4 * j + v, 1)] = (uint8_t)(w >> 16);
-    }
+    for (int i = 0; i < 8; ++i)
+      dst[tile_col(t, l, 4 * j + i / 2, i % 2)] = (uint8_t)plane_index<Q>(pl, 4 * (i / 4) + j, i % 4);
   }
 }
 

@@ -188,13 +188,15 @@ __device__ __forceinline__ void compute_int(const Group<B0, false> &g0, const Gr
   }
 }
 
-// Decoded B operand of step j from the merged bit-plane indices and the
-// lane's row LUT.
+// Decoded B operand of step j from the top q planes and the lane's row LUT
+// (byte-split: low bytes of the entries, then high bytes): two quads of
+// four weights, each looked up by byte permutes.
 template <int Q>
 __device__ __forceinline__ f16x8 plane_bop(const uint32_t *tp, int j, const uint32_t *L) {
-  const uint32_t m = plane_merge<Q>(tp, j);
-  return pack_b(lut_pair<Q>(m & 0x000F000Fu, L), lut_pair<Q>((m >> 4) & 0x000F000Fu, L),
-                lut_pair<Q>((m >> 8) & 0x000F000Fu, L), lut_pair<Q>((m >> 12) & 0x000F000Fu, L));
+  uint32_t d[4];
+  plane_quad<Q>(tp, j, L, d[0], d[1]);
+  plane_quad<Q>(tp, 4 + j, L, d[2], d[3]);
+  return pack_b(d[0], d[1], d[2], d[3]);
 }
 
 template <int Q>
@@ -313,13 +315,19 @@ __device__ __forceinline__ void lut_load(const BlockDesc &d, int strip, int g4, 
   for (int i = 0; i < NQ / 2; ++i) ls.v[i] = gld<uint32_t>(p + 2 * i);
 }
 
+// Stored byte-split for the permute lookups: the row's 2^q low bytes
+// (entry i in byte i) in 2^q / 4 dwords, then its 2^q high bytes.
 template <int Q>
 __device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, int c) {
   (void)c;
   constexpr int NQ = 1 << Q;
   const int lane = threadIdx.x & 63;
+  uint32_t *row = reinterpret_cast<uint32_t *>(dst + lane * NQ);
 #pragma unroll
-  for (int i = 0; i < NQ / 2; ++i) reinterpret_cast<uint32_t *>(dst + lane * NQ)[i] = ls.v[i];
+  for (int m = 0; m < NQ / 4; ++m) {
+    row[m] = __builtin_amdgcn_perm(ls.v[2 * m + 1], ls.v[2 * m], 0x06040200u);
+    row[NQ / 4 + m] = __builtin_amdgcn_perm(ls.v[2 * m + 1], ls.v[2 * m], 0x07050301u);
+  }
 }
 
 // z of the chunk's pairs in LDS: sums the ks fp32 partials of the
