@@ -16,8 +16,9 @@ struct Ws {
   int ks_gu, ks_d;
 };
 
-// Kernel path of one call.  Tiled: INT blocks, on average >= 64 pairs per
-// expert, shapes the tiled kernels cover (H a multiple of 256, 32-bit
+// Kernel path of one call.  Tiled: INT blocks, on average >= 384 pairs per
+// expert (below that, streaming the weights once per 32-token chunk is as
+// fast or faster on a Mixtral-sized layer), shapes the tiled kernels cover (H a multiple of 256, 32-bit
 // element offsets of the activation rows, z rows that fit one activation
 // buffer); weight streaming otherwise.
 static bool tiled_fits(const moeq_layer *L, int T, int k) {
@@ -34,7 +35,7 @@ static int pick_path(const moeq_layer *L, int T, int k, const moeq_ffn_options *
   if (want == MOEQ_PATH_STREAM) return MOEQ_PATH_STREAM;
   if (want != MOEQ_PATH_AUTO) return -1;
   const int64_t P = (int64_t)T * k;
-  return (tiled_fits(L, T, k) && P >= 64ll * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
+  return (tiled_fits(L, T, k) && P >= 384ll * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
 }
 
 static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
@@ -134,7 +135,7 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.nsub_max = std::max(1, std::min(kMT, T) / 16 + (std::min(kMT, T) % 16 ? 1 : 0));
   if (a.comp_on) {
     prof_begin("lowrank_project_gu", stream);
-    launch_lowrank_project(a, 0, dim3(mc * 4, 2 * a.RZ / 16), stream);
+    launch_lowrank_project(a, 0, dim3(mc * kSubPerChunk, 2 * a.RZ / 16), stream);
     prof_end("lowrank_project_gu", stream);
   }
   const bool tiled = path == MOEQ_PATH_TILED;
@@ -150,7 +151,7 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   }
   if (a.comp_on) {
     prof_begin("lowrank_project_down", stream);
-    launch_lowrank_project(a, 1, dim3(mc * 4, a.RZ / 16), stream);
+    launch_lowrank_project(a, 1, dim3(mc * kSubPerChunk, a.RZ / 16), stream);
     prof_end("lowrank_project_down", stream);
   }
   if (tiled) {

@@ -6,7 +6,12 @@
 
 namespace moeq {
 
-constexpr int kMT = 64;            // tokens per chunk (up to four 16-row MFMA tiles)
+// Tokens per chunk of the weight-streaming kernels (up to two 16-row MFMA
+// tiles).  A 64-token class (four tiles) needs twice the LDS and registers,
+// which leaves one or two workgroups per CU; two 32-token chunks that each
+// read the weights are faster at every size measured.
+constexpr int kMT = 32;
+constexpr int kSubPerChunk = kMT / 16;   // 16-token tiles per chunk
 constexpr int kTiledM = 128;       // tokens per token tile of the tiled kernels
 constexpr int kStripsPerWG = 4;    // one 16-row strip per wave
 

@@ -16,14 +16,14 @@ namespace moeq {
 // tokens leave no K split: each activation fragment then feeds both jobs,
 // so the activations are read half as often); 4 waves split the range and
 // reduce through LDS in fixed order.
-// grid.x = max_chunks * 4 tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ,
+// grid.x = max_chunks * kSubPerChunk tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ,
 // grid.z = ks.  mode 0: v = x[token] (gate/up blocks); mode 1: v = h[pos]
 // (down block).
 template <int NJ>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode) {
   __shared__ f32x4 s_part[4][NJ][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int chunk = blockIdx.x / 4, sub = blockIdx.x % 4;
+  const int chunk = blockIdx.x / kSubPerChunk, sub = blockIdx.x % kSubPerChunk;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch)) return;
   if (16 * sub >= ch.cnt) return;

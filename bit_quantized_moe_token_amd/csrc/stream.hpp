@@ -5,7 +5,7 @@
 // the low-rank terms fused into the expert pass.
 //
 // A workgroup = 4 waves = 4 strips of 16 output rows of one expert, for one
-// chunk of up to 64 of the expert's tokens (NSUB 16-row MFMA tiles).  Every
+// chunk of up to 32 of the expert's tokens (NSUB 16-row MFMA tiles).  Every
 // packed weight is read from HBM exactly once per chunk.  K is walked in
 // groups of four 128-column tiles:
 //   - the group's activations (NSUB*16 rows x 512 columns, rows gathered by
@@ -610,8 +610,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, true);
   const int row = strip * 16 + (lane & 15);
-  // first U operands (gate, up), requested before the K walk where the
-  // registers allow (not in the 64-token class)
+  // first U operands (gate, up), requested before the K walk
   constexpr bool kPreU = NSUB <= 2;
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
   if (kPreU && a.comp_on && a.r > 0) {
@@ -674,8 +673,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, false);
-  // first U operands of the two strips, requested before the K walk where
-  // the registers allow (not in the 64-token class)
+  // first U operands of the two strips, requested before the K walk
   constexpr bool kPreU = NSUB <= 2;
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
   if (kPreU && epi && a.r > 0) {
@@ -717,13 +715,12 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
   return moeq_dyn_lds;
 }
 
-// Chunk classes by token tiles: NSUB = 1 when no chunk can exceed 16
-// tokens, else 2 (up to 32 tokens, the smaller chunks included: one launch
-// fewer costs less than their idle MFMA rows) and 4 (up to 64).  One
-// launch per class present; a workgroup whose chunk is of another class
-// exits at once.
+// Chunk class by token tiles: NSUB = 1 when no chunk can exceed 16 tokens,
+// else 2 (up to 32 tokens, the smaller chunks included: one launch fewer
+// costs less than their idle MFMA rows).  One launch per call.
 __device__ __forceinline__ int class_of(int cnt, int nsub_max) {
-  return nsub_max == 1 ? 1 : (cnt <= 32 ? 2 : 4);
+  (void)cnt;
+  return nsub_max == 1 ? 1 : 2;
 }
 
 // LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
@@ -735,7 +732,7 @@ inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
 
 // gate/up: 256 threads; grid.x = max_chunks * (I / 64)
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) gateup_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 3) gateup_kernel(FfnArgs a) {
   uint16_t *lds = dyn_lds();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_sg = a.I / 64;
@@ -759,7 +756,7 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) gate
 
 // down: 256 threads, 128 rows; grid.x = max_chunks * (H / 128) * splits
 template <int NSUB, int GPT, bool PLANE>
-__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : (NSUB == 2 ? 3 : 1)) down_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 3) down_kernel(FfnArgs a) {
   uint16_t *lds = dyn_lds();
   const int n_sg = a.H / 128;
   const int split = blockIdx.x % a.splits;
@@ -781,8 +778,6 @@ void launch_gateup_class(const FfnArgs &a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((gateup_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
   else
     hipLaunchKernelGGL((gateup_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
-  if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((gateup_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
 }
 
 template <int GPT, bool PLANE>
@@ -791,8 +786,6 @@ void launch_down_class(const FfnArgs &a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((down_kernel<1, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 1, a.RZ), s, a);
   else
     hipLaunchKernelGGL((down_kernel<2, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 2, a.RZ), s, a);
-  if (a.nsub_max >= 3)
-    hipLaunchKernelGGL((down_kernel<4, GPT, PLANE>), dim3(grid), dim3(256), stream_lds_bytes(PLANE, 4, a.RZ), s, a);
 }
 
 void launch_gateup_g128(const FfnArgs &a, int grid, hipStream_t s);

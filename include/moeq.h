@@ -320,8 +320,9 @@ moeq_status moeq_route_mass(const moeq_routing *r, int32_t T, int32_t E, int32_t
 
 typedef enum {
   MOEQ_PATH_AUTO = 0,   /* chosen from the average tokens per expert          */
-  MOEQ_PATH_STREAM = 1, /* weight-streaming: each weight read once per call,
-                           tokens of one expert in 16-row MFMA tiles           */
+  MOEQ_PATH_STREAM = 1, /* weight-streaming: each weight read once per chunk
+                           of up to 32 of an expert's tokens (16-row MFMA
+                           tiles)                                              */
   MOEQ_PATH_VALU = 2,   /* weight-streaming with fp32 VALU dot products only   */
   MOEQ_PATH_TILED = 3   /* LDS-tiled grouped GEMM for many tokens per expert   */
 } moeq_path;

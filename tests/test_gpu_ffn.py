@@ -17,7 +17,9 @@ pytestmark = pytest.mark.gpu
 CASES = {
     "tiny": ("tiny", {}),
     "decode": ("decode", dict(H=512, I=1792)),
-    "prefill": ("prefill", dict(H=512, I=1792, T=1024)),
+    # T = 1536, k = 2, E = 8: 384 pairs per expert on average, where the
+    # default path turns from streaming to tiled
+    "prefill": ("prefill", dict(H=512, I=1792, T=1536)),
     "finegrained": ("finegrained", {}),
     "bitplane": ("bitplane", dict(E=32, T=128)),
     # the largest expert count (256): experts with one or two pairs, chunk
@@ -140,15 +142,23 @@ def test_ffn_tiled_path_matches_oracle(case):
 
 
 def test_ffn_prefill_paths():
-    """The batch of the prefill workload takes the tiled path by default;
-    the streaming path gives the same result within the tolerance."""
+    """The default path is the tiled one from an average of 384 pairs per
+    expert (this batch) and the streaming one below (its first 1024
+    tokens); each path gives the oracle's result within the tolerance."""
     cfg, orc, dev, x, logits = _setup("prefill")
+    assert cfg["T"] * cfg["k"] == 384 * cfg["E"]
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
     auto = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
     tiled = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
     assert torch.equal(auto, tiled)
     stream = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
     layers.check_y(stream.cpu().numpy(), ref, "prefill stream")
+    small = dict(cfg, T=1024)
+    xs, ls = x[:1024].copy(), logits[:1024].copy()
+    auto_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32)
+    stream_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
+    assert torch.equal(auto_s, stream_s)
+    layers.check_y(auto_s.cpu().numpy(), layers.oracle_y(orc, small, xs, ls, cfg["n_comp"]), "prefill T=1024 auto")
     perm = np.random.default_rng(7).permutation(cfg["T"])
     tp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32,
               path=PATH_TILED)
