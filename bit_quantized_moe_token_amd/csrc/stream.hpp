@@ -611,9 +611,8 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   row_ptrs<NSUB, 4>(rowp, a, ch, true);
   const int row = strip * 16 + (lane & 15);
   // first U operands (gate, up), requested before the K walk
-  constexpr bool kPreU = NSUB <= 2;
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
-  if (kPreU && a.comp_on && a.r > 0) {
+  if (a.comp_on && a.r > 0) {
     ub[0] = lowrank_bop(dg.U, a.r, row, 0);
     ub[1] = lowrank_bop(du.U, a.r, row, 0);
   }
@@ -629,10 +628,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const BlockDesc &d = b ? du : dg;
-      if (a.r > 0) {
-        if (kPreU) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b], ub[b]);
-        else lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b]);
-      }
+      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[b], ub[b]);
       if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[b]);
     }
   }
@@ -674,9 +670,8 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
   row_ptrs<NSUB, 4>(rowp, a, ch, false);
   // first U operands of the two strips, requested before the K walk
-  constexpr bool kPreU = NSUB <= 2;
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
-  if (kPreU && epi && a.r > 0) {
+  if (epi && a.r > 0) {
     ub[0] = lowrank_bop(d.U, a.r, st0 * 16 + (lane & 15), 0);
     ub[1] = lowrank_bop(d.U, a.r, st1 * 16 + (lane & 15), 0);
   }
@@ -693,10 +688,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   for (int b = 0; b < 2; ++b) {
     const int row = (b ? st1 : st0) * 16 + (lane & 15);
     if (epi) {
-      if (a.r > 0) {
-        if (kPreU) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b], ub[b]);
-        else lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b]);
-      }
+      if (a.r > 0) lowrank_epi<NSUB>(d.U, a.r, a.Rp, row, zs, zw, acc[b], ub[b]);
       if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + a.Rp, zw, acc[b]);
     }
 #pragma unroll
@@ -718,10 +710,7 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
 // Chunk class by token tiles: NSUB = 1 when no chunk can exceed 16 tokens,
 // else 2 (up to 32 tokens, the smaller chunks included: one launch fewer
 // costs less than their idle MFMA rows).  One launch per call.
-__device__ __forceinline__ int class_of(int cnt, int nsub_max) {
-  (void)cnt;
-  return nsub_max == 1 ? 1 : 2;
-}
+__device__ __forceinline__ int chunk_class(int nsub_max) { return nsub_max == 1 ? 1 : 2; }
 
 // LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
 inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
@@ -733,12 +722,13 @@ inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
 // gate/up: 256 threads; grid.x = max_chunks * (I / 64)
 template <int NSUB, int GPT, bool PLANE>
 __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 3) gateup_kernel(FfnArgs a) {
+  static_assert(NSUB == 1 || NSUB == 2, "chunks hold at most 32 tokens");
   uint16_t *lds = dyn_lds();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_sg = a.I / 64;
   const int chunk = blockIdx.x / n_sg, sg = blockIdx.x % n_sg;
   Chunk ch;
-  if (!find_chunk(a.offsets, a.E, chunk, &ch) || class_of(ch.cnt, a.nsub_max) != NSUB) return;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || chunk_class(a.nsub_max) != NSUB) return;
   const int strip = 4 * sg + wave;
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
@@ -757,13 +747,14 @@ __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 3) gateup_kernel(FfnArgs 
 // down: 256 threads, 128 rows; grid.x = max_chunks * (H / 128) * splits
 template <int NSUB, int GPT, bool PLANE>
 __global__ void __launch_bounds__(256, NSUB == 1 ? 4 : 3) down_kernel(FfnArgs a) {
+  static_assert(NSUB == 1 || NSUB == 2, "chunks hold at most 32 tokens");
   uint16_t *lds = dyn_lds();
   const int n_sg = a.H / 128;
   const int split = blockIdx.x % a.splits;
   const int rest = blockIdx.x / a.splits;
   const int chunk = rest / n_sg, sg = rest % n_sg;
   Chunk ch;
-  if (!find_chunk(a.offsets, a.E, chunk, &ch) || class_of(ch.cnt, a.nsub_max) != NSUB) return;
+  if (!find_chunk(a.offsets, a.E, chunk, &ch) || chunk_class(a.nsub_max) != NSUB) return;
   switch (a.desc[3 * ch.e + 2].bits) {
     case 2: down_body<NSUB, GPT, PLANE, 2>(a, ch, sg, split, lds); break;
     case 3: down_body<NSUB, GPT, PLANE, 3>(a, ch, sg, split, lds); break;
