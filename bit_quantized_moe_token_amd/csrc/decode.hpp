@@ -26,10 +26,11 @@
 //     it gives c x 2^-24 exactly inside the MFMA (streaming kernels).
 // Bit-plane packing (4 bytes per plane per lane per tile): the bit of code
 // plane c for register element i = 2v + h of step j (pair P = 4j + v, half
-// h) is at bit 8 (i mod 4) + 4 (i div 4) + j.  The four weights of a quad
-// (elements 4qd .. 4qd + 3 of a step) thus sit at the same bit s = 4qd + j
-// of the four bytes, so one shift and one mask per plane spread a quad's
-// indices one per byte: the byte selectors of v_perm.
+// h) is at bit 8 (i mod 4) + 4 (i div 4) + j, rotated left by c.  The four
+// weights of a quad (elements 4qd .. 4qd + 3 of a step) thus sit at bit
+// s + c of the four bytes (s = 4qd + j), so a mask per plane and one
+// rotation of their OR put a quad's indices one per byte, plane c at bit c
+// (then down by 4 - q): the byte selectors of v_perm.
 #pragma once
 #include "common.hpp"
 
@@ -204,28 +205,22 @@ __device__ __forceinline__ f16x8 rescale_a(f16x8 a) {
 // Bit of element i (0..7) of step j in a plane dword.
 __host__ __device__ constexpr int plane_bit(int j, int i) { return 8 * (i % 4) + 4 * (i / 4) + j; }
 
-// x >> d for d >= 0, x << -d otherwise (d folds to a constant once the
-// step loops are unrolled).
-__device__ __forceinline__ uint32_t shift_r(uint32_t x, int d) { return d >= 0 ? x >> d : x << -d; }
-
 // The low min(q, 3) bits of the q-bit indices of a quad, weight e in byte
-// e, from the top q planes (pl[0] = plane 3, the index's most significant
-// bit); s = 4 qd + j.
+// e, from the top q planes (pl[u] = plane 3 - u; plane c is index bit
+// c - (4 - q)); s = 4 qd + j.
 template <int Q>
 __device__ __forceinline__ uint32_t plane_sel(const uint32_t *pl, int s) {
-  uint32_t sel = 0;
+  uint32_t t = 0;
 #pragma unroll
-  for (int u = Q > 3 ? 1 : 0; u < Q; ++u) {
-    const int b = Q - 1 - u;
-    sel |= shift_r(pl[u], s - b) & (0x01010101u << b);
-  }
-  return sel;
+  for (int u = Q > 3 ? 1 : 0; u < Q; ++u) t |= pl[u] & __builtin_rotateleft32(0x01010101u, s + 3 - u);
+  return __builtin_rotateright32(t, s + 4 - Q);
 }
 
 // q = 4: selector that takes byte e from the entries-8..15 lookup when
-// index bit 3 of weight e is set, else from the entries-0..7 lookup.
+// index bit 3 of weight e (plane 3) is set, else from the entries-0..7
+// lookup.
 __device__ __forceinline__ uint32_t plane_top(const uint32_t *pl, int s) {
-  return (shift_r(pl[0], s - 2) & 0x04040404u) | 0x03020100u;
+  return __builtin_rotateright32(pl[0] & __builtin_rotateleft32(0x01010101u, s + 3), s + 1) | 0x03020100u;
 }
 
 // Full q-bit index of weight e of a quad (debug read-back).

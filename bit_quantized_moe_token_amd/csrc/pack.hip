@@ -70,7 +70,7 @@ pack_planes_kernel(const uint8_t *__restrict__ codes, int N, int K, uint8_t *__r
     for (int h = 0; h < 2; ++h) {
       const uint32_t c = src[tile_col(t, l, P, h)] & 15u;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) pl[b] |= ((c >> b) & 1u) << plane_bit(j, 2 * v + h);
+      for (int b = 0; b < 4; ++b) pl[b] |= ((c >> b) & 1u) << ((plane_bit(j, 2 * v + h) + b) & 31);
     }
   }
   const uint64_t off = code_offset(s, t, l, n_kt, 4);
