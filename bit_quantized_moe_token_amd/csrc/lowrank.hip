@@ -12,10 +12,10 @@ namespace moeq {
 
 // Partial z[pos][slot] = V v over one K range for compensated pairs (zero
 // for the others); the consumer kernels sum the ks partials in fixed order.
-// One 16-token tile and NJ 16-column jobs per workgroup (NJ = 2 when many
-// tokens leave no K split: each activation fragment then feeds both jobs,
-// so the activations are read half as often); 4 waves split the range and
-// reduce through LDS in fixed order.
+// One 16-token tile and NJ 16-column jobs per workgroup (NJ = 2, 4 or 8
+// when many tokens leave no K split: each activation fragment then feeds
+// every job, so the activations are read NJ times less often); 4 waves
+// split the range and reduce through LDS in fixed order.
 // grid.x = max_chunks * kSubPerChunk tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ,
 // grid.z = ks.  mode 0: v = x[token] (gate/up blocks); mode 1: v = h[pos]
 // (down block).
@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
   // batches of BATCH steps: all their fragment loads are issued before the
   // first MFMA, so each batch waits for memory once
-  constexpr int BATCH = 8 / NJ;
+  constexpr int BATCH = NJ >= 8 ? 2 : 8 / NJ;
   const f16x8 zero = pack_b(0, 0, 0, 0);
   f32x4 acc[NJ], acc2[NJ];
 #pragma unroll
@@ -197,10 +197,13 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
   grid.z = mode == 0 ? a.ks_gu : a.ks_d;
-  // two (four, from eight jobs up) jobs per workgroup when many tokens
-  // leave no K split (the activation re-reads dominate; fewer jobs keep
-  // enough workgroups); the job count is always even
-  if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) {
+  // two, four or eight jobs per workgroup when many tokens leave no K
+  // split (the activation re-reads dominate; fewer jobs keep enough
+  // workgroups); the job count is always even
+  if (a.P > 256 && grid.z == 1 && grid.y % 8 == 0) {
+    grid.y /= 8;
+    hipLaunchKernelGGL(lowrank_project_kernel<8>, grid, dim3(256), 0, s, a, mode);
+  } else if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) {
     grid.y /= 4;
     hipLaunchKernelGGL(lowrank_project_kernel<4>, grid, dim3(256), 0, s, a, mode);
   } else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) {
