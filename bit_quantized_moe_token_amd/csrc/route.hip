@@ -250,11 +250,24 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t
   const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
   for (int e = tid; e < E; e += kSegThreads) { s_tot[e] = 0; s_base[e] = 0; s_run[e] = 0; }
   __syncthreads();
-#pragma unroll 4
-  for (int p = tid; p < P; p += kSegThreads) {
-    const int e = ids[p];
-    atomicAdd(&s_tot[e], 1);
-    if (p < p0) atomicAdd(&s_base[e], 1);
+  // ids in batches of 16 per thread: a batch's loads are all requested
+  // before its first counter update, so it waits for memory once
+  constexpr int kCountBatch = 16;
+  for (int q = 0; q < P; q += kCountBatch * kSegThreads) {
+    int ev[kCountBatch];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int p = q + u * kSegThreads + tid;
+      ev[u] = p < P ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int p = q + u * kSegThreads + tid;
+      if (ev[u] >= 0) {
+        atomicAdd(&s_tot[ev[u]], 1);
+        if (p < p0) atomicAdd(&s_base[ev[u]], 1);
+      }
+    }
   }
   __syncthreads();
   if (wave == 0) {
