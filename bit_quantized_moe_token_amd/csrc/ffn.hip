@@ -16,9 +16,9 @@ struct Ws {
   int ks_gu, ks_d;
 };
 
-// Kernel path of one call.  Tiled: INT blocks, on average >= 384 pairs per
-// expert (below that, streaming the weights once per 32-token chunk is as
-// fast or faster on a Mixtral-sized layer), shapes the tiled kernels cover (H a multiple of 256, 32-bit
+// Kernel path of one call.  Tiled: INT blocks, on average at least
+// tiled_min_pairs per expert (below that, streaming the weights once per
+// 32-token chunk is as fast or faster on a Mixtral-sized layer), shapes the tiled kernels cover (H a multiple of 256, 32-bit
 // element offsets of the activation rows, z rows that fit one activation
 // buffer); weight streaming otherwise.
 static bool tiled_fits(const moeq_layer *L, int T, int k) {
@@ -29,13 +29,23 @@ static bool tiled_fits(const moeq_layer *L, int T, int k) {
          (int64_t)T * D.H < (1ll << 31) && P * D.I < (1ll << 31) && 2 * RZ <= kTileK + 8;
 }
 
+// Average pairs per expert from which the tiled path is faster, measured on
+// the Mixtral-sized layer (E = 8, k = 2): about 96 for int4 (T = 384) and
+// 384 for int3 (T = 1536), whose fields cost the tiled decode more; layers
+// with any block below 4 bits take the larger figure.
+static int64_t tiled_min_pairs(const moeq_layer *L) {
+  for (uint8_t b : L->bits)
+    if (b != 4) return 384;
+  return 96;
+}
+
 static int pick_path(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
   const int want = o ? o->path : MOEQ_PATH_AUTO;
   if (want == MOEQ_PATH_TILED) return tiled_fits(L, T, k) ? MOEQ_PATH_TILED : -1;
   if (want == MOEQ_PATH_STREAM) return MOEQ_PATH_STREAM;
   if (want != MOEQ_PATH_AUTO) return -1;
   const int64_t P = (int64_t)T * k;
-  return (tiled_fits(L, T, k) && P >= 384ll * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
+  return (tiled_fits(L, T, k) && P >= tiled_min_pairs(L) * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
 }
 
 static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {

@@ -17,8 +17,7 @@ pytestmark = pytest.mark.gpu
 CASES = {
     "tiny": ("tiny", {}),
     "decode": ("decode", dict(H=512, I=1792)),
-    # T = 1536, k = 2, E = 8: 384 pairs per expert on average, where the
-    # default path turns from streaming to tiled
+    # int4, T = 1536, k = 2, E = 8: 384 pairs per expert on average
     "prefill": ("prefill", dict(H=512, I=1792, T=1536)),
     "finegrained": ("finegrained", {}),
     "bitplane": ("bitplane", dict(E=32, T=128)),
@@ -142,23 +141,24 @@ def test_ffn_tiled_path_matches_oracle(case):
 
 
 def test_ffn_prefill_paths():
-    """The default path is the tiled one from an average of 384 pairs per
-    expert (this batch) and the streaming one below (its first 1024
-    tokens); each path gives the oracle's result within the tolerance."""
+    """For an int4 layer the default path is the tiled one from an average
+    of 96 pairs per expert (this batch) and the streaming one below (its
+    first 256 tokens, 64 pairs per expert); each path gives the oracle's
+    result within the tolerance."""
     cfg, orc, dev, x, logits = _setup("prefill")
-    assert cfg["T"] * cfg["k"] == 384 * cfg["E"]
+    assert cfg["fmt"] == "int" and cfg["bits"] == 4 and cfg["T"] * cfg["k"] >= 96 * cfg["E"]
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
     auto = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
     tiled = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
     assert torch.equal(auto, tiled)
     stream = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
     layers.check_y(stream.cpu().numpy(), ref, "prefill stream")
-    small = dict(cfg, T=1024)
-    xs, ls = x[:1024].copy(), logits[:1024].copy()
+    small = dict(cfg, T=256)
+    xs, ls = x[:256].copy(), logits[:256].copy()
     auto_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32)
     stream_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
     assert torch.equal(auto_s, stream_s)
-    layers.check_y(auto_s.cpu().numpy(), layers.oracle_y(orc, small, xs, ls, cfg["n_comp"]), "prefill T=1024 auto")
+    layers.check_y(auto_s.cpu().numpy(), layers.oracle_y(orc, small, xs, ls, cfg["n_comp"]), "prefill T=256 auto")
     perm = np.random.default_rng(7).permutation(cfg["T"])
     tp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32,
               path=PATH_TILED)
