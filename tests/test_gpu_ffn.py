@@ -19,6 +19,8 @@ CASES = {
     "decode": ("decode", dict(H=512, I=1792)),
     # int4, T = 1536, k = 2, E = 8: 384 pairs per expert on average
     "prefill": ("prefill", dict(H=512, I=1792, T=1536)),
+    # the int3 layer with as many tokens (where its default turns tiled)
+    "decode_many": ("decode", dict(H=512, I=1792, T=1536)),
     "finegrained": ("finegrained", {}),
     "bitplane": ("bitplane", dict(E=32, T=128)),
     # the largest expert count (256): experts with one or two pairs, chunk
@@ -163,6 +165,23 @@ def test_ffn_prefill_paths():
     tp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32,
               path=PATH_TILED)
     assert torch.equal(tp, tiled[torch.from_numpy(perm).cuda()])
+
+
+def test_ffn_default_path_int3():
+    """A layer with 3-bit blocks takes the tiled path only from an average of
+    384 pairs per expert (this batch); at 256 (its first 1024 tokens) it
+    streams."""
+    cfg, orc, dev, x, logits = _setup("decode_many")
+    assert cfg["bits"] == 3 and cfg["T"] * cfg["k"] == 384 * cfg["E"]
+    auto = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    tiled = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
+    assert torch.equal(auto, tiled)
+    layers.check_y(auto.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"]), "int3 T=1536 auto")
+    small = dict(cfg, T=1024)
+    xs, ls = x[:1024].copy(), logits[:1024].copy()
+    auto_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32)
+    stream_s = _run(dev, small, xs, ls, cfg["n_comp"], out_dtype=torch.float32, path=PATH_STREAM)
+    assert torch.equal(auto_s, stream_s)
 
 
 def test_ffn_tiled_unsupported_for_bitplane():
