@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 FMT_INT, FMT_BITPLANE = 0, 1
 F16, F32 = 0, 1
-PATH_AUTO, PATH_STREAM, PATH_VALU, PATH_TILED = 0, 1, 2, 3
+PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 3
 
 c_void_p = ctypes.c_void_p
 c_size_t = ctypes.c_size_t

@@ -139,6 +139,76 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// ---- power-of-two normalisation of fp16 activations.  Activations (x)
+// and the SwiGLU output (h) are held in fp16 scaled by an exact power of
+// two so that their largest magnitude per token (per pair for h) lies in
+// [2^kNormTop, 2^(kNormTop+1)): their relative precision then does not
+// depend on their absolute size.  The scale is undone in fp32.
+constexpr int kNormTop = 6;
+constexpr int kNoExp = -1000;   // exponent of an all-zero row or block
+
+// floor(log2 |v|) of a finite float (denormals included); kNoExp for 0.
+__device__ __forceinline__ int ilogb_f32(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v) & 0x7fffffffu;
+  if (b == 0) return kNoExp;
+  const int e = (int)(b >> 23);
+  return e ? e - 127 : (31 - __builtin_clz(b)) - 149;
+}
+
+// floor(log2 m) of an fp16 magnitude given by its bits (sign cleared).
+__device__ __forceinline__ int ilogb_f16bits(uint32_t m) {
+  if (m == 0) return kNoExp;
+  const int e = (int)(m >> 10);
+  return e ? e - 15 : (31 - __builtin_clz(m)) - 24;
+}
+
+// Exponent K of x~ = x * 2^K for a token whose largest |x| has
+// floor(log2) = e: the largest lands in [2^kNormTop, 2^(kNormTop+1)).  K is
+// capped at 15 so that 2^K stays an fp16 number (rows whose largest value
+// is below 2^(kNormTop-15) are scaled by 2^15 and stay smaller).
+__device__ __forceinline__ int x_norm_exp(int e) { return e >= kNormTop - 15 ? kNormTop - e : 15; }
+
+// fp16 bits of 2^e for e <= 15 (subnormal from -15 down to -24; 0 below).
+__host__ __device__ constexpr uint32_t f16_pow2_bits(int e) {
+  return e < -24 ? 0u : e < -14 ? (1u << (e + 24)) : (uint32_t)(e + 15) << 10;
+}
+
+// (2^e, 2^e) as an fp16 pair, e <= 15.
+__device__ __forceinline__ uint32_t f16x2_pow2(int e) { return f16_pow2_bits(e) * 0x10001u; }
+
+// Multiply the eight fp16 values of v by the fp16 pair m (exact for powers
+// of two unless the result is subnormal).
+// (The elements go through as_h2 by value: a bit_cast applied directly to
+// a vector-element expression v[i] reads element 0 with this compiler.)
+__device__ __forceinline__ u32x4 scale_f16x8(u32x4 v, uint32_t m) {
+  const f16x2 mm = as_h2(m);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = as_u32(as_h2(v[i]) * mm);
+  return r;
+}
+
+// Largest value over the 16 lanes of each DPP row.
+template <typename T>
+__device__ __forceinline__ T dpp_row_max(T v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  auto step = [](T x, int ctrl_sel) {
+    int xi = __builtin_bit_cast(int, x), yi;
+    switch (ctrl_sel) {
+      case 0: yi = __builtin_amdgcn_mov_dpp(xi, 0xb1, 0xf, 0xf, true); break;    // quad_perm [1,0,3,2]
+      case 1: yi = __builtin_amdgcn_mov_dpp(xi, 0x4e, 0xf, 0xf, true); break;    // quad_perm [2,3,0,1]
+      case 2: yi = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xf, 0xf, true); break;   // row_half_mirror
+      default: yi = __builtin_amdgcn_mov_dpp(xi, 0x140, 0xf, 0xf, true); break;  // row_mirror
+    }
+    const T y = __builtin_bit_cast(T, yi);
+    return x > y ? x : y;
+  };
+  v = step(v, 0);
+  v = step(v, 1);
+  v = step(v, 2);
+  return step(v, 3);
+}
+
 // Round a float64 to the nearest fp16 (ties to even), directly from the
 // double's bits so there is exactly one rounding.  Finite inputs only.
 __host__ __device__ inline uint16_t f64_to_f16_bits(double d) {

@@ -1,8 +1,9 @@
 // Host entry of the routed expert FFN: workspace layout, launch plan and
 // the sequence of kernels on the caller's stream (no host synchronisation).
 //
-//   project V x (gate/up) -> gate/up stream + SwiGLU -> project V_down h
-//   -> down stream (split-K partials) -> gate-weighted combine
+//   project V x (gate/up) + x exponents -> gate/up + SwiGLU (h with block
+//   exponents) -> project V_down h + h renormalised per pair -> down
+//   (split-K partials) -> gate-weighted combine (undoes the h exponent)
 #include "common.hpp"
 #include "ffn.hpp"
 #include "layer.hpp"
@@ -12,7 +13,7 @@ namespace moeq {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
-  size_t zp_gu, zp_d, h, ypart, total;
+  size_t zp_gu, zp_d, h, hblk, hn, hexp, xexp, ypart, total;
   int ks_gu, ks_d;
 };
 
@@ -76,6 +77,10 @@ static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
   w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * P * 2 * RZ * 4);
   w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
   w.h = off; off = al256(off + (size_t)P * L->dims.I * 2);
+  w.hblk = off; off = al256(off + (size_t)P * (L->dims.I / 64) * 4);
+  w.hn = off; off = al256(off + (size_t)P * L->dims.I * 2);
+  w.hexp = off; off = al256(off + (size_t)P * 4);
+  w.xexp = off; off = al256(off + (size_t)T * 4);
   w.ypart = off; off = al256(off + (size_t)splits * P * L->dims.H * 4);
   w.total = off;
   return w;
@@ -135,6 +140,10 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.ks_stride_gu = (int64_t)T * k * 2 * a.RZ;
   a.ks_stride_d = (int64_t)T * k * a.RZ;
   a.h = reinterpret_cast<uint16_t *>(wb + w.h);
+  a.hblk = reinterpret_cast<int32_t *>(wb + w.hblk);
+  a.hn = reinterpret_cast<uint16_t *>(wb + w.hn);
+  a.hexp = reinterpret_cast<int32_t *>(wb + w.hexp);
+  a.xexp = reinterpret_cast<int32_t *>(wb + w.xexp);
   a.ypart = reinterpret_cast<float *>(wb + w.ypart);
   a.splits = splits;
   a.P = T * k;
@@ -143,10 +152,15 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.G = D.G;
   a.fmt = D.fmt;
   a.nsub_max = std::max(1, std::min(kMT, T) / 16 + (std::min(kMT, T) % 16 ? 1 : 0));
+  // x exponents (with the gate/up projection when there is one)
   if (a.comp_on) {
     prof_begin("lowrank_project_gu", stream);
     launch_lowrank_project(a, 0, dim3(mc * kSubPerChunk, 2 * a.RZ / 16), stream);
     prof_end("lowrank_project_gu", stream);
+  } else {
+    prof_begin("xexp", stream);
+    launch_xexp(a, stream);
+    prof_end("xexp", stream);
   }
   const bool tiled = path == MOEQ_PATH_TILED;
   const int mt = tiled ? max_chunks(D.E, T, k, kTiledM) : 0;     // token tiles of the tiled path
@@ -159,10 +173,16 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
     launch_gateup_stream(a, mc * (D.I / 64), stream);
     prof_end("gateup_stream", stream);
   }
+  // h renormalised to one exponent per pair (with the down projection when
+  // there is one)
   if (a.comp_on) {
     prof_begin("lowrank_project_down", stream);
     launch_lowrank_project(a, 1, dim3(mc * kSubPerChunk, a.RZ / 16), stream);
     prof_end("lowrank_project_down", stream);
+  } else {
+    prof_begin("hnorm", stream);
+    launch_hnorm(a, stream);
+    prof_end("hnorm", stream);
   }
   if (tiled) {
     prof_begin("down_tiled", stream);

@@ -30,8 +30,12 @@ struct FfnArgs {
   float *zp_d;      // [ks_d][P][RZ] fp32 partial V_down h
   int ks_gu, ks_d;  // K splits of the two projections
   int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
-  uint16_t *h;      // [P][I] fp16
-  float *ypart;     // [splits][P][H] fp32
+  uint16_t *h;      // [P][I] fp16: h * 2^(kNormTop - eb), eb per (pair, 64-row block of I)
+  int32_t *hblk;    // [P][I/64] eb: floor(log2) of the block's largest |h| (kNoExp if all zero)
+  uint16_t *hn;     // [P][I] fp16: h * 2^(kNormTop - eh), eh = the pair's largest eb
+  int32_t *hexp;    // [P] eh
+  int32_t *xexp;    // [T] K: the gate/up kernels work on x * 2^K (x_norm_exp)
+  float *ypart;     // [splits][P][H] fp32, in units of 2^(eh - kNormTop) (the combine undoes it)
   int splits;
   int P;
   int nsub_max;     // largest number of 16-token tiles a chunk can have
@@ -81,6 +85,48 @@ __device__ __forceinline__ f16x8 load_a(const uint16_t *p) {
   return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
+// ---- activation normalisation (see kNormTop).
+
+// x exponents K_t of tokens t = wid, wid + nw, ...: one wave per token
+// takes the largest |x| of the row (fp16 magnitude bits compare as
+// integers) and writes x_norm_exp of its exponent.
+__device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int t = wid; t < a.T; t += nw) {
+    const uint16_t *row = a.x + (int64_t)t * a.H;
+    uint32_t m = 0;
+    for (int c = 8 * lane; c < a.H; c += 8 * kWave) {
+      const u32x4 v = gld<u32x4>(row + c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) m = std::max(m, std::max(v[w] & 0x7fffu, (v[w] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) m = std::max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    if (lane == 0) a.xexp[t] = x_norm_exp(ilogb_f16bits(m));
+  }
+}
+
+// K of chunk row m (rows past the chunk's count repeat its last token).
+__device__ __forceinline__ int row_kx(const FfnArgs &a, const Chunk &ch, int m) {
+  const int p = a.sorted_pairs[ch.base + std::min(m, ch.cnt - 1)];
+  return a.xexp[p / a.k];
+}
+
+// eh of 16 pairs (sorted positions pos0 .. pos0 + 15, clamped to
+// pos_last), computed by the workgroup's 256 threads into s_eh[16]: thread
+// tid takes row tid / 16 and every 16th block from tid % 16, then a DPP
+// row maximum.  The caller synchronises before reading s_eh.
+__device__ __forceinline__ void pair_eh16(const FfnArgs &a, int pos0, int pos_last, int *s_eh) {
+  const int tid = threadIdx.x;
+  const int r = tid >> 4, nb = a.I / 64;
+  const int pos = std::min(pos0 + r, pos_last);
+  const int32_t *src = a.hblk + (int64_t)pos * nb;
+  int e = kNoExp;
+  for (int j = tid & 15; j < nb; j += 16) e = std::max(e, (int)gld<int32_t>(src + j));
+  e = dpp_row_max(e);
+  if ((tid & 15) == 0) s_eh[r] = e;
+}
+
 // Upper bound of the number of chunks of MT pairs for T tokens, top-k, E
 // experts (an expert holds at most T pairs).
 inline int max_chunks(int E, int T, int k, int MT = kMT) {
@@ -96,6 +142,8 @@ void launch_gateup_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_down_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s);
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s);
+void launch_xexp(const FfnArgs &a, hipStream_t s);    // x exponents alone (no gate/up projection)
+void launch_hnorm(const FfnArgs &a, hipStream_t s);   // h renormalisation alone (no down projection)
 void launch_tiled_gateup(const FfnArgs &a, int grid, hipStream_t s);   // tiled_gu.hip
 void launch_tiled_down(const FfnArgs &a, int grid, hipStream_t s);     // tiled_dn.hip
 

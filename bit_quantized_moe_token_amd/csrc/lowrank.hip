@@ -16,17 +16,34 @@ namespace moeq {
 // when many tokens leave no K split: each activation fragment then feeds
 // every job, so the activations are read NJ times less often); 4 waves
 // split the range and reduce through LDS in fixed order.
-// grid.x = max_chunks * kSubPerChunk tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ,
-// grid.z = ks.  mode 0: v = x[token] (gate/up blocks); mode 1: v = h[pos]
-// (down block).
+// grid.x = max_chunks * kSubPerChunk tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ
+// (+ 1 in mode 0), grid.z = ks.  mode 0: v = x[token] (gate/up blocks);
+// the extra y slice (blockIdx.y == njy) computes the tokens' x exponents
+// instead.  mode 1: v = h of the pair, renormalised on the fly from its
+// per-block exponents to the pair's exponent eh; the workgroups of y slice
+// 0 also store that renormalised h (hn) and eh, which the down kernels and
+// the combine read.
 template <int NJ>
-__global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode) {
+__global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy) {
   __shared__ f32x4 s_part[4][NJ][64];
+  __shared__ int s_eh[16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (mode == 0 && (int)blockIdx.y >= njy) {
+    xexp_rows(a, ((int)blockIdx.z * (int)gridDim.x + (int)blockIdx.x) * 4 + wave, (int)(gridDim.x * gridDim.z) * 4);
+    return;
+  }
   const int chunk = blockIdx.x / kSubPerChunk, sub = blockIdx.x % kSubPerChunk;
   Chunk ch;
   if (!find_chunk(a.offsets, a.E, chunk, &ch)) return;
   if (16 * sub >= ch.cnt) return;
+  // mode 1: eh of the tile's 16 pairs; y slice 0 writes hn and eh
+  const bool write_hn = mode == 1 && blockIdx.y == 0;
+  if (mode == 1) {
+    pair_eh16(a, ch.base + 16 * sub, ch.base + ch.cnt - 1, s_eh);
+    __syncthreads();
+    if (write_hn && blockIdx.z == 0 && threadIdx.x < 16 && 16 * sub + (int)threadIdx.x < ch.cnt)
+      a.hexp[ch.base + 16 * sub + threadIdx.x] = s_eh[threadIdx.x];
+  }
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
   const int K = mode == 0 ? a.H : a.I;
   const int KS = mode == 0 ? a.ks_gu : a.ks_d;
@@ -54,6 +71,8 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     vi[j] = live[j] && i < R;
     vrow[j] = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
   }
+  // (y slice 0 always holds a live job: rank tile 0 of the first factor set
+  // with a nonzero rank, so the workgroups that store hn never exit here)
   if (!any) {
     if (wave == 0)
 #pragma unroll
@@ -70,6 +89,20 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const uint16_t *arow = (mode == 0) ? a.x + (int64_t)(a.sorted_pairs[pos] / a.k) * a.H
                                      : a.h + (int64_t)pos * a.I;
   arow += 8 * (lane >> 4);
+  // mode 1: the lane's row of h is renormalised per 64-column block by
+  // 2^(eb - eh) (32-column steps st lie in block st / 2); y slice 0 stores
+  // the result for the rows of the chunk
+  const int eh = mode == 1 ? s_eh[lane & 15] : 0;
+  const int32_t *ebrow = a.hblk + (int64_t)pos * (a.I / 64);
+  uint16_t *hnrow = a.hn + (int64_t)pos * a.I + 8 * (lane >> 4);
+  const bool store_hn = write_hn && 16 * sub + (lane & 15) < ch.cnt;
+  auto frag = [&](int st) -> f16x8 {
+    const f16x8 v = load_a(arow + 32 * st);
+    if (mode == 0) return v;
+    const u32x4 w = scale_f16x8(__builtin_bit_cast(u32x4, v), f16x2_pow2(gld<int32_t>(ebrow + (st >> 1)) - eh));
+    if (store_hn) *reinterpret_cast<u32x4 *>(hnrow + 32 * st) = w;
+    return __builtin_bit_cast(f16x8, w);
+  };
   const int nsteps = K / 32;
   const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
   const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
@@ -85,7 +118,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     f16x8 av[BATCH], bv[BATCH][NJ];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      av[u] = load_a(arow + 32 * (st + u));
+      av[u] = frag(st + u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bv[u][j] = vi[j] ? load_a(vrow[j] + 32 * (st + u)) : zero;
     }
@@ -98,7 +131,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
       }
   }
   for (; st < s1; ++st) {
-    const f16x8 av = load_a(arow + 32 * st);
+    const f16x8 av = frag(st);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = mfma16(av, vi[j] ? load_a(vrow[j] + 32 * st) : zero, acc[j]);
   }
@@ -134,8 +167,9 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   }
 }
 
-// y[t] = sum_j g[t][j] * sum_s ypart[s][pair_pos[t*k+j]], slots in order,
-// splits in order within a slot; one thread per (token, 4 columns).  Slots
+// y[t] = sum_j g[t][j] * 2^(eh - kNormTop) * sum_s ypart[s][pair_pos[t*k+j]],
+// slots in order, splits in order within a slot; one thread per (token, 4
+// columns); eh is the h exponent of the pair (see hexp).  Slots
 // go in groups of 4: their gates and positions are loaded together, then
 // every partial of the group (up to MS splits each; MS = 1 when there is
 // one split, so that the many-token case keeps few registers) is requested
@@ -156,8 +190,9 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const bool ok = j0 + jj < a.k;
-      g[jj] = ok ? a.gates[tk + j0 + jj] : 0.f;
       pos[jj] = ok ? a.pair_pos[tk + j0 + jj] : 0;
+      // y_pair is held in units of 2^(eh - kNormTop) of its pair
+      g[jj] = ok ? __builtin_ldexpf(a.gates[tk + j0 + jj], a.hexp[pos[jj]] - kNormTop) : 0.f;
     }
     f32x4 v[4][MS];
 #pragma unroll
@@ -200,18 +235,51 @@ void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s
   // two, four or eight jobs per workgroup when many tokens leave no K
   // split (the activation re-reads dominate; fewer jobs keep enough
   // workgroups); the job count is always even
-  if (a.P > 256 && grid.z == 1 && grid.y % 8 == 0) {
-    grid.y /= 8;
-    hipLaunchKernelGGL(lowrank_project_kernel<8>, grid, dim3(256), 0, s, a, mode);
-  } else if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) {
-    grid.y /= 4;
-    hipLaunchKernelGGL(lowrank_project_kernel<4>, grid, dim3(256), 0, s, a, mode);
-  } else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) {
-    grid.y /= 2;
-    hipLaunchKernelGGL(lowrank_project_kernel<2>, grid, dim3(256), 0, s, a, mode);
-  } else {
-    hipLaunchKernelGGL(lowrank_project_kernel<1>, grid, dim3(256), 0, s, a, mode);
+  int nj = 1;
+  if (a.P > 256 && grid.z == 1 && grid.y % 8 == 0) nj = 8;
+  else if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) nj = 4;
+  else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) nj = 2;
+  grid.y /= nj;
+  const int njy = (int)grid.y;
+  if (mode == 0) grid.y += 1;                 // the x-exponent slice
+  switch (nj) {
+    case 8: hipLaunchKernelGGL(lowrank_project_kernel<8>, grid, dim3(256), 0, s, a, mode, njy); break;
+    case 4: hipLaunchKernelGGL(lowrank_project_kernel<4>, grid, dim3(256), 0, s, a, mode, njy); break;
+    case 2: hipLaunchKernelGGL(lowrank_project_kernel<2>, grid, dim3(256), 0, s, a, mode, njy); break;
+    default: hipLaunchKernelGGL(lowrank_project_kernel<1>, grid, dim3(256), 0, s, a, mode, njy); break;
   }
+}
+
+// x exponents when no gate/up projection runs: one wave per token.
+__global__ void __launch_bounds__(256) xexp_kernel(FfnArgs a) {
+  xexp_rows(a, (int)blockIdx.x * 4 + (threadIdx.x >> 6), (int)gridDim.x * 4);
+}
+
+// hn and eh when no down projection runs: 16 pairs (sorted positions) per
+// workgroup; each thread rescales 16-byte pieces of the rows.
+__global__ void __launch_bounds__(256) hnorm_kernel(FfnArgs a) {
+  __shared__ int s_eh[16];
+  const int pos0 = (int)blockIdx.x * 16;
+  pair_eh16(a, pos0, a.P - 1, s_eh);
+  __syncthreads();
+  if (threadIdx.x < 16 && pos0 + (int)threadIdx.x < a.P) a.hexp[pos0 + threadIdx.x] = s_eh[threadIdx.x];
+  const int per_row = a.I / 8, nb = a.I / 64;
+  for (int i = threadIdx.x; i < 16 * per_row; i += 256) {
+    const int r = i / per_row, c = (i % per_row) * 8;
+    const int pos = pos0 + r;
+    if (pos >= a.P) break;
+    const int64_t off = (int64_t)pos * a.I + c;
+    const int eb = gld<int32_t>(a.hblk + (int64_t)pos * nb + c / 64);
+    *reinterpret_cast<u32x4 *>(a.hn + off) = scale_f16x8(gld<u32x4>(a.h + off), f16x2_pow2(eb - s_eh[r]));
+  }
+}
+
+void launch_xexp(const FfnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(xexp_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+}
+
+void launch_hnorm(const FfnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(hnorm_kernel, dim3((a.P + 15) / 16), dim3(256), 0, s, a);
 }
 
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s) {

@@ -88,6 +88,9 @@ constexpr int kTBBytes = 16 * 1024;
 constexpr int kTMetaBytes = 4 * 512;                  // per wave: 64 lanes x 2 dword slots
 constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
 constexpr int kTStages = 3;
+constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
+// dynamic LDS of a tiled launch: the stages, then the gate/up rows' x exponents
+constexpr size_t kTiledLdsLaunch = kTiledLdsBytes + kTM * 4;
 
 // DMA operations per strip per tile: one 16-byte transfer for 4-bit codes,
 // else one 4-byte transfer per code dword.
@@ -258,6 +261,8 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
     rowoff[i] = (uint32_t)(a.sorted_pairs[ch.base + m] / a.k) * (uint32_t)a.H;
   }
+  // the rows' x exponents, past the LDS stages (published by the K loop's barriers)
+  if (threadIdx.x < kTM) reinterpret_cast<int *>(lds + kTiledLdsBytes)[threadIdx.x] = row_kx(a, ch, threadIdx.x);
   f32x4 acc[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -286,11 +291,22 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     ub[q] = a.comp_on && a.r > 0 ? lowrank_bop((q >> 1) ? du.U : dg.U, a.r, strips[q] * 16 + (lane & 15), 0)
                                  : pack_b(0, 0, 0, 0);
   kl.template run<8>(acc);
+  // acc holds W x; with compensation it is moved to the units of the
+  // normalised x~ = x 2^K before the low-rank terms (z rows hold V x~)
+  const int *s_kx = reinterpret_cast<const int *>(lds + kTiledLdsBytes);
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int K = s_kx[16 * s + 4 * (lane >> 4) + i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q][s][i] = __builtin_ldexpf(acc[q][s][i], K);
+      }
     uint16_t *zs = l16;
-    if (zpre) z_store<8, 4, 8>(zp, zw, zs);
-    else z_prologue<8, 4>(a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    if (zpre) z_store<8, 4, 8>(a, ch, zp, zw, zs);
+    else z_prologue<8, 4>(a, true, a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -302,19 +318,45 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     }
     __syncthreads();
   }
-  // h = SiLU(gate) * up into LDS [128 tokens][128 columns], then coalesced rows
-  uint16_t *hs = l16;
+  // h = SiLU(gate) * up, then per token the largest |h| over the
+  // workgroup's 128 columns (lanes of a DPP row, then the 4 waves)
+  float *s_hmax = reinterpret_cast<float *>(lds + kTM * kTS * 2);     // [4][128], past the h tile
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int col = 32 * wave + 16 * g + (lane & 15);
+  for (int s = 0; s < 8; ++s) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * s + 4 * (lane >> 4) + i;
+      const int K = a.comp_on ? -s_kx[m] : 0;
+      float mx = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = acc[g][s][i], uv = acc[2 + g][s][i];
+      for (int g = 0; g < 2; ++g) {
+        const float gv = __builtin_ldexpf(acc[g][s][i], K), uv = __builtin_ldexpf(acc[2 + g][s][i], K);
         const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        hs[(16 * s + 4 * (lane >> 4) + i) * kTS + col] = __builtin_bit_cast(uint16_t, (f16)hv);
+        acc[g][s][i] = hv;
+        mx = std::max(mx, __builtin_fabsf(hv));
       }
+      mx = dpp_row_max(mx);
+      if ((lane & 15) == 0) s_hmax[wave * kTM + m] = mx;
+    }
+  }
+  __syncthreads();
+  // h 2^(kNormTop - eb) into LDS [128 tokens][128 columns], then coalesced rows
+  uint16_t *hs = l16;
+  const int nb = a.I / 64;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * s + 4 * (lane >> 4) + i;
+      const float mx = std::max(std::max(s_hmax[m], s_hmax[kTM + m]), std::max(s_hmax[2 * kTM + m], s_hmax[3 * kTM + m]));
+      const int eb = ilogb_f32(mx);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int col = 32 * wave + 16 * g + (lane & 15);
+        hs[m * kTS + col] = __builtin_bit_cast(uint16_t, (f16)__builtin_ldexpf(acc[g][s][i], kNormTop - eb));
+      }
+      if (wave == 0 && (lane & 15) < 2 && m < ch.cnt)
+        a.hblk[(int64_t)(ch.base + m) * nb + 2 * nt + (lane & 15)] = eb;
     }
   }
   __syncthreads();
@@ -340,7 +382,7 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
-    rowoff[i] = (uint32_t)(ch.base + m) * (uint32_t)a.I;
+    rowoff[i] = (uint32_t)(ch.base + m) * (uint32_t)a.I;       // rows of the normalised h
   }
   f32x4 acc[4][8];
 #pragma unroll
@@ -349,11 +391,11 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.codes, code_region_bytes(d));
   const TKLoop<BD, BD, GPT> kl{d, d, strips, a.I / kTileK, wave, rowoff, lds,
-                               make_rsrc(a.h, (uint32_t)a.P * (uint32_t)a.I * 2u), rc, rc};
+                               make_rsrc(a.hn, (uint32_t)a.P * (uint32_t)a.I * 2u), rc, rc};
   kl.template run<8>(acc);
   if (a.comp_on) {
     uint16_t *zs = reinterpret_cast<uint16_t *>(lds);
-    z_prologue<8, 4>(a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
+    z_prologue<8, 4>(a, false, a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -416,6 +458,6 @@ __global__ void __launch_bounds__(256, 1) tiled_down_kernel(FfnArgs a) {
   }
 }
 
-constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
+
 
 }  // namespace moeq

@@ -323,7 +323,7 @@ typedef enum {
   MOEQ_PATH_STREAM = 1, /* weight-streaming: each weight read once per chunk
                            of up to 32 of an expert's tokens (16-row MFMA
                            tiles)                                              */
-  MOEQ_PATH_VALU = 2,   /* weight-streaming with fp32 VALU dot products only   */
+  /* 2 is reserved (MOEQ_ERR_UNSUPPORTED)                                     */
   MOEQ_PATH_TILED = 3   /* LDS-tiled grouped GEMM for many tokens per expert   */
 } moeq_path;
 

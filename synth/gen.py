@@ -12,7 +12,10 @@ key, so that changing T (or drawing fewer rows) never shifts any other draw:
   [seed, 6]                      outlier activation channels
   [seed, 7, grp, blk, 0|1]       shared compensator factors U | V, N(0, 0.01)
 
-"N(0, s)" is read as mean 0 and standard deviation s.  Blocks are numbered
+"N(0, s)" is read as mean 0 and standard deviation s.  Two optional config
+keys move a layer across the fp16 range without changing any draw: x_scale
+multiplies the activations and w_scale the expert weights (both before the
+rounding to fp16).  Blocks are numbered
 0 = gate, 1 = up, 2 = down; gate/up blocks are [I, H] (rows = outputs), down
 is [H, I].  Values are rounded to the storage type (fp16 weights, activations
 and factors, fp32 logits) here, and those rounded values are the inputs of
@@ -48,7 +51,7 @@ def _weight_chunk(cfg, seed, e, blk, chunk):
     r0 = chunk * ROW_CHUNK
     rows = min(ROW_CHUNK, n - r0)
     a = _rng(seed, 2, e, blk, chunk).standard_normal((rows, kdim), dtype=np.float32)
-    a *= np.float32(0.02)
+    a *= np.float32(0.02 * float(cfg.get("w_scale", 1.0)))
     return a.astype(np.float16)
 
 
@@ -123,6 +126,7 @@ def gen_x(cfg, seed):
     ch = outlier_channels(cfg, seed)
     if len(ch):
         x[:, ch] *= float(cfg["outlier_mult"])
+    x *= float(cfg.get("x_scale", 1.0))
     return x.astype(np.float16)
 
 
