@@ -75,6 +75,9 @@ SIGNATURES = [
     ("moeq_ffn_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions), ctypes.POINTER(c_size_t)]),
     ("moeq_expert_ffn", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
                                 c_void_p, c_i32, c_void_p, c_size_t, ctypes.POINTER(FfnOptions), c_void_p]),
+    ("moeq_ffn_noalloc_max_bytes", c_i32, [ctypes.POINTER(c_size_t)]),
+    ("moeq_expert_ffn_noalloc", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
+                                        c_void_p, c_i32, ctypes.POINTER(FfnOptions), c_void_p]),
     ("moeq_profile_enable", c_i32, [c_i32]),
     ("moeq_profile_read", c_i32, [c_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_i32),
                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32)]),

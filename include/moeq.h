@@ -355,6 +355,26 @@ moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int32_t T,
                             void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
                             const moeq_ffn_options *opts, hipStream_t stream);
 
+/*
+ * moeq_expert_ffn_noalloc — moeq_expert_ffn for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments (minus the workspace), same kernels and bit-identical results;
+ * the working memory is a fixed array of moeq_ffn_noalloc_max_bytes bytes
+ * (64 MiB) that the library holds in every GPU it runs on until the
+ * process ends.  The call allocates nothing (its first call on a device
+ * looks up that device's array).  A call whose working memory
+ * (moeq_ffn_workspace_size) exceeds the array returns MOEQ_ERR_WORKSPACE
+ * before anything is enqueued.  All calls on one GPU share the array:
+ * calls that can overlap on one GPU (several streams, several threads)
+ * race and must be ordered by the caller.
+ */
+moeq_status moeq_ffn_noalloc_max_bytes(size_t *bytes);
+moeq_status moeq_expert_ffn_noalloc(const moeq_layer *L, const uint16_t *x, int32_t T,
+                                    int32_t k, const moeq_routing *r, int32_t n_comp,
+                                    void *y, int32_t y_dtype, const moeq_ffn_options *opts,
+                                    hipStream_t stream);
+
 /* ---------------------------------------------------------- profiling -- */
 
 /*
