@@ -173,8 +173,12 @@ __host__ __device__ constexpr uint32_t f16_pow2_bits(int e) {
   return e < -24 ? 0u : e < -14 ? (1u << (e + 24)) : (uint32_t)(e + 15) << 10;
 }
 
-// (2^e, 2^e) as an fp16 pair, e <= 15.
-__device__ __forceinline__ uint32_t f16x2_pow2(int e) { return f16_pow2_bits(e) * 0x10001u; }
+// (2^e, 2^e) as an fp16 pair, e <= 15 (0 below 2^-24): the fp32 power of
+// two converted once (exact; 2^-25 and below round to 0).
+__device__ __forceinline__ uint32_t f16x2_pow2(int e) {
+  const f16 h = (f16)__builtin_ldexpf(1.0f, e);
+  return as_u32(f16x2{h, h});
+}
 
 // Multiply the eight fp16 values of v by the fp16 pair m (exact for powers
 // of two unless the result is subnormal).
@@ -188,25 +192,28 @@ __device__ __forceinline__ u32x4 scale_f16x8(u32x4 v, uint32_t m) {
   return r;
 }
 
-// Largest value over the 16 lanes of each DPP row.
-template <typename T>
-__device__ __forceinline__ T dpp_row_max(T v) {
-  static_assert(sizeof(T) == 4, "32-bit values");
-  auto step = [](T x, int ctrl_sel) {
-    int xi = __builtin_bit_cast(int, x), yi;
-    switch (ctrl_sel) {
-      case 0: yi = __builtin_amdgcn_mov_dpp(xi, 0xb1, 0xf, 0xf, true); break;    // quad_perm [1,0,3,2]
-      case 1: yi = __builtin_amdgcn_mov_dpp(xi, 0x4e, 0xf, 0xf, true); break;    // quad_perm [2,3,0,1]
-      case 2: yi = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xf, 0xf, true); break;   // row_half_mirror
-      default: yi = __builtin_amdgcn_mov_dpp(xi, 0x140, 0xf, 0xf, true); break;  // row_mirror
-    }
-    const T y = __builtin_bit_cast(T, yi);
-    return x > y ? x : y;
-  };
-  v = step(v, 0);
-  v = step(v, 1);
-  v = step(v, 2);
-  return step(v, 3);
+// Largest value over the 16 lanes of each DPP row (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ float dpp_row_max(float v) {
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0xb1>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4e>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, v))));
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0x140>(__builtin_bit_cast(int, v))));
+}
+__device__ __forceinline__ float dpp_half_row_max(float v) {   // over the 8 lanes of each half-row
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0xb1>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4e>(__builtin_bit_cast(int, v))));
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, v))));
+}
+__device__ __forceinline__ int dpp_row_max(int v) {
+  v = __builtin_elementwise_max(v, dpp_i<0xb1>(v));
+  v = __builtin_elementwise_max(v, dpp_i<0x4e>(v));
+  v = __builtin_elementwise_max(v, dpp_i<0x141>(v));
+  return __builtin_elementwise_max(v, dpp_i<0x140>(v));
 }
 
 // Round a float64 to the nearest fp16 (ties to even), directly from the

@@ -13,7 +13,7 @@ namespace moeq {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
-  size_t zp_gu, zp_d, h, hblk, hn, hexp, xexp, ypart, total;
+  size_t zp_gu, zp_d, h, hblk, hn, hexp, xexp, xn, ypart, total;
   int ks_gu, ks_d;
 };
 
@@ -66,6 +66,8 @@ static int pick_ks(int P, int K) {
   return std::max(1, std::min(16, K / 1024));
 }
 
+static int hblk_stride(const moeq_layer *L) { return (L->dims.I / 64 + 15) / 16 * 16; }
+
 static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
   const int64_t P = (int64_t)T * k;
   const int Rp = (L->dims.r + 31) / 32 * 32, Rsp = (L->dims.rs + 31) / 32 * 32;
@@ -77,10 +79,11 @@ static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
   w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * P * 2 * RZ * 4);
   w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
   w.h = off; off = al256(off + (size_t)P * L->dims.I * 2);
-  w.hblk = off; off = al256(off + (size_t)P * (L->dims.I / 64) * 4);
+  w.hblk = off; off = al256(off + (size_t)P * hblk_stride(L));
   w.hn = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.hexp = off; off = al256(off + (size_t)P * 4);
-  w.xexp = off; off = al256(off + (size_t)T * 4);
+  w.xexp = off; off = al256(off + (size_t)P * 4);
+  w.xn = off; off = al256(off + (size_t)T * L->dims.H * 2);
   w.ypart = off; off = al256(off + (size_t)splits * P * L->dims.H * 4);
   w.total = off;
   return w;
@@ -117,6 +120,7 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   if (!x || !y || !r->topk_gates || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
     return fail(MOEQ_ERR_INVALID, "expert_ffn: null pointer");
   const int splits = pick_splits(L, T, k, opts);
+  const bool tiled = path == MOEQ_PATH_TILED;
   const Ws w = ws_plan(L, T, k, splits);
   if (!ws || ws_bytes < w.total)
     return fail(MOEQ_ERR_WORKSPACE, "expert_ffn: workspace has %zu bytes, needs %zu", ws_bytes, w.total);
@@ -140,10 +144,12 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.ks_stride_gu = (int64_t)T * k * 2 * a.RZ;
   a.ks_stride_d = (int64_t)T * k * a.RZ;
   a.h = reinterpret_cast<uint16_t *>(wb + w.h);
-  a.hblk = reinterpret_cast<int32_t *>(wb + w.hblk);
+  a.hblk = reinterpret_cast<int8_t *>(wb + w.hblk);
+  a.hblk_stride = hblk_stride(L);
   a.hn = reinterpret_cast<uint16_t *>(wb + w.hn);
   a.hexp = reinterpret_cast<int32_t *>(wb + w.hexp);
   a.xexp = reinterpret_cast<int32_t *>(wb + w.xexp);
+  a.xn = reinterpret_cast<uint16_t *>(wb + w.xn);
   a.ypart = reinterpret_cast<float *>(wb + w.ypart);
   a.splits = splits;
   a.P = T * k;
@@ -152,7 +158,8 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   a.G = D.G;
   a.fmt = D.fmt;
   a.nsub_max = std::max(1, std::min(kMT, T) / 16 + (std::min(kMT, T) % 16 ? 1 : 0));
-  // x exponents (with the gate/up projection when there is one)
+  // x exponents and the normalised x * 2^K that the gate/up kernels read
+  // (with the gate/up projection when there is one)
   if (a.comp_on) {
     prof_begin("lowrank_project_gu", stream);
     launch_lowrank_project(a, 0, dim3(mc * kSubPerChunk, 2 * a.RZ / 16), stream);
@@ -162,7 +169,6 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
     launch_xexp(a, stream);
     prof_end("xexp", stream);
   }
-  const bool tiled = path == MOEQ_PATH_TILED;
   const int mt = tiled ? max_chunks(D.E, T, k, kTiledM) : 0;     // token tiles of the tiled path
   if (tiled) {
     prof_begin("gateup_tiled", stream);

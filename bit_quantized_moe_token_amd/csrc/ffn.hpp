@@ -31,10 +31,12 @@ struct FfnArgs {
   int ks_gu, ks_d;  // K splits of the two projections
   int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
   uint16_t *h;      // [P][I] fp16: h * 2^(kNormTop - eb), eb per (pair, 64-row block of I)
-  int32_t *hblk;    // [P][I/64] eb: floor(log2) of the block's largest |h| (kNoExp if all zero)
+  int8_t *hblk;     // [P][hblk_stride] eb (h_block_exp), I/64 used per row
+  int hblk_stride;  // bytes per row of hblk (I/64 rounded up to 16)
   uint16_t *hn;     // [P][I] fp16: h * 2^(kNormTop - eh), eh = the pair's largest eb
   int32_t *hexp;    // [P] eh
-  int32_t *xexp;    // [T] K: the gate/up kernels work on x * 2^K (x_norm_exp)
+  int32_t *xexp;    // [P] K of the pair's token, by sorted position (x_norm_exp)
+  uint16_t *xn;     // [T][H] x * 2^K, the activations the gate/up kernels read
   float *ypart;     // [splits][P][H] fp32, in units of 2^(eh - kNormTop) (the combine undoes it)
   int splits;
   int P;
@@ -87,9 +89,20 @@ __device__ __forceinline__ f16x8 load_a(const uint16_t *p) {
 
 // ---- activation normalisation (see kNormTop).
 
-// x exponents K_t of tokens t = wid, wid + nw, ...: one wave per token
-// takes the largest |x| of the row (fp16 magnitude bits compare as
-// integers) and writes x_norm_exp of its exponent.
+// Exponent of a block of h with largest magnitude mx, as stored (int8):
+// floor(log2 mx) clamped to [-127, 127], kHZero (-128) for an all-zero
+// block.  h 2^(kNormTop - eb) then has its largest magnitude in
+// [2^kNormTop, 2^(kNormTop+1)) (smaller where the clamp applies).
+constexpr int kHZero = -128;
+__device__ __forceinline__ int h_block_exp(float mx) {
+  const int e = ilogb_f32(mx);
+  return e == kNoExp ? kHZero : std::max(-127, std::min(127, e));
+}
+
+// x exponents of tokens t = wid, wid + nw, ...: one wave per token takes
+// the largest |x| of the row (fp16 magnitude bits compare as integers),
+// writes K = x_norm_exp of its exponent to the token's k sorted positions
+// and the row x 2^K to xn.
 __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   const int lane = threadIdx.x & 63;
   for (int t = wid; t < a.T; t += nw) {
@@ -102,27 +115,35 @@ __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
     }
 #pragma unroll
     for (int o = 32; o; o >>= 1) m = std::max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
-    if (lane == 0) a.xexp[t] = x_norm_exp(ilogb_f16bits(m));
+    const int K = x_norm_exp(ilogb_f16bits(m));
+    for (int j = lane; j < a.k; j += kWave) a.xexp[a.pair_pos[(int64_t)t * a.k + j]] = K;
+    const uint32_t mul = f16x2_pow2(K);
+    uint16_t *out = a.xn + (int64_t)t * a.H;
+    for (int c = 8 * lane; c < a.H; c += 8 * kWave)
+      *reinterpret_cast<u32x4 *>(out + c) = scale_f16x8(gld<u32x4>(row + c), mul);
   }
 }
 
-// K of chunk row m (rows past the chunk's count repeat its last token).
-__device__ __forceinline__ int row_kx(const FfnArgs &a, const Chunk &ch, int m) {
-  const int p = a.sorted_pairs[ch.base + std::min(m, ch.cnt - 1)];
-  return a.xexp[p / a.k];
-}
-
 // eh of 16 pairs (sorted positions pos0 .. pos0 + 15, clamped to
-// pos_last), computed by the workgroup's 256 threads into s_eh[16]: thread
-// tid takes row tid / 16 and every 16th block from tid % 16, then a DPP
-// row maximum.  The caller synchronises before reading s_eh.
-__device__ __forceinline__ void pair_eh16(const FfnArgs &a, int pos0, int pos_last, int *s_eh) {
+// pos_last), computed by the workgroup's 256 threads: thread tid takes row
+// tid / 16 and, per 256 blocks, 16 consecutive block exponents (one 16-byte
+// load; blocks past I/64 ignored), then a DPP row maximum into s_eh[16].
+// With s_eb (used when I/64 <= 256) the exponents are also kept in LDS,
+// s_eb[row * 256 + block].  The caller synchronises before reading them.
+__device__ __forceinline__ void pair_eh16(const FfnArgs &a, int pos0, int pos_last, int *s_eh, int8_t *s_eb) {
   const int tid = threadIdx.x;
   const int r = tid >> 4, nb = a.I / 64;
   const int pos = std::min(pos0 + r, pos_last);
-  const int32_t *src = a.hblk + (int64_t)pos * nb;
-  int e = kNoExp;
-  for (int j = tid & 15; j < nb; j += 16) e = std::max(e, (int)gld<int32_t>(src + j));
+  int e = kHZero;
+  for (int j0 = 16 * (tid & 15); j0 < nb; j0 += 256) {
+    const u32x4 v = gld<u32x4>(a.hblk + (int64_t)pos * a.hblk_stride + j0);
+    if (s_eb) *reinterpret_cast<u32x4 *>(s_eb + r * 256 + j0) = v;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int eb = (int)(int8_t)(v[b >> 2] >> (8 * (b & 3)));
+      if (j0 + b < nb) e = std::max(e, eb);
+    }
+  }
   e = dpp_row_max(e);
   if ((tid & 15) == 0) s_eh[r] = e;
 }

@@ -27,6 +27,7 @@ template <int NJ>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy) {
   __shared__ f32x4 s_part[4][NJ][64];
   __shared__ int s_eh[16];
+  __shared__ __attribute__((aligned(16))) int8_t s_eb[16 * 256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (mode == 0 && (int)blockIdx.y >= njy) {
     xexp_rows(a, ((int)blockIdx.z * (int)gridDim.x + (int)blockIdx.x) * 4 + wave, (int)(gridDim.x * gridDim.z) * 4);
@@ -38,8 +39,9 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   if (16 * sub >= ch.cnt) return;
   // mode 1: eh of the tile's 16 pairs; y slice 0 writes hn and eh
   const bool write_hn = mode == 1 && blockIdx.y == 0;
+  const bool eb_lds = a.I / 64 <= 256;
   if (mode == 1) {
-    pair_eh16(a, ch.base + 16 * sub, ch.base + ch.cnt - 1, s_eh);
+    pair_eh16(a, ch.base + 16 * sub, ch.base + ch.cnt - 1, s_eh, eb_lds ? s_eb : nullptr);
     __syncthreads();
     if (write_hn && blockIdx.z == 0 && threadIdx.x < 16 && 16 * sub + (int)threadIdx.x < ch.cnt)
       a.hexp[ch.base + 16 * sub + threadIdx.x] = s_eh[threadIdx.x];
@@ -93,13 +95,12 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   // 2^(eb - eh) (32-column steps st lie in block st / 2); y slice 0 stores
   // the result for the rows of the chunk
   const int eh = mode == 1 ? s_eh[lane & 15] : 0;
-  const int32_t *ebrow = a.hblk + (int64_t)pos * (a.I / 64);
+  const int8_t *ebrow = eb_lds ? s_eb + (lane & 15) * 256 : a.hblk + (int64_t)pos * a.hblk_stride;
   uint16_t *hnrow = a.hn + (int64_t)pos * a.I + 8 * (lane >> 4);
   const bool store_hn = write_hn && 16 * sub + (lane & 15) < ch.cnt;
-  auto frag = [&](int st) -> f16x8 {
-    const f16x8 v = load_a(arow + 32 * st);
-    if (mode == 0) return v;
-    const u32x4 w = scale_f16x8(__builtin_bit_cast(u32x4, v), f16x2_pow2(gld<int32_t>(ebrow + (st >> 1)) - eh));
+  // mode 1: h fragment of step st renormalised to eh (and stored by slice 0)
+  auto renorm = [&](f16x8 v, int st) -> f16x8 {
+    const u32x4 w = scale_f16x8(__builtin_bit_cast(u32x4, v), f16x2_pow2((int)ebrow[st >> 1] - eh));
     if (store_hn) *reinterpret_cast<u32x4 *>(hnrow + 32 * st) = w;
     return __builtin_bit_cast(f16x8, w);
   };
@@ -118,10 +119,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     f16x8 av[BATCH], bv[BATCH][NJ];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      av[u] = frag(st + u);
+      av[u] = load_a(arow + 32 * (st + u));
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bv[u][j] = vi[j] ? load_a(vrow[j] + 32 * (st + u)) : zero;
     }
+    if (mode == 1)
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) av[u] = renorm(av[u], st + u);
 #pragma unroll
     for (int u = 0; u < BATCH; u += 2)
 #pragma unroll
@@ -131,7 +135,8 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
       }
   }
   for (; st < s1; ++st) {
-    const f16x8 av = frag(st);
+    f16x8 av = load_a(arow + 32 * st);
+    if (mode == 1) av = renorm(av, st);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = mfma16(av, vi[j] ? load_a(vrow[j] + 32 * st) : zero, acc[j]);
   }
@@ -260,16 +265,16 @@ __global__ void __launch_bounds__(256) xexp_kernel(FfnArgs a) {
 __global__ void __launch_bounds__(256) hnorm_kernel(FfnArgs a) {
   __shared__ int s_eh[16];
   const int pos0 = (int)blockIdx.x * 16;
-  pair_eh16(a, pos0, a.P - 1, s_eh);
+  pair_eh16(a, pos0, a.P - 1, s_eh, nullptr);
   __syncthreads();
   if (threadIdx.x < 16 && pos0 + (int)threadIdx.x < a.P) a.hexp[pos0 + threadIdx.x] = s_eh[threadIdx.x];
-  const int per_row = a.I / 8, nb = a.I / 64;
+  const int per_row = a.I / 8;
   for (int i = threadIdx.x; i < 16 * per_row; i += 256) {
     const int r = i / per_row, c = (i % per_row) * 8;
     const int pos = pos0 + r;
     if (pos >= a.P) break;
     const int64_t off = (int64_t)pos * a.I + c;
-    const int eb = gld<int32_t>(a.hblk + (int64_t)pos * nb + c / 64);
+    const int eb = gld<int8_t>(a.hblk + (int64_t)pos * a.hblk_stride + c / 64);
     *reinterpret_cast<u32x4 *>(a.hn + off) = scale_f16x8(gld<u32x4>(a.h + off), f16x2_pow2(eb - s_eh[r]));
   }
 }

@@ -31,6 +31,7 @@
 namespace moeq {
 
 constexpr int kXStride = 4 * kTileK + 8;   // halves per staged activation row
+constexpr int kH32Stream = 64 + 4;          // floats per row of the gate/up epilogue's fp32 h tile
 
 // Staging buffers per class: the 16-token INT class (occupancy 4 by
 // registers) has LDS to spare for two, which saves one barrier per tile
@@ -272,16 +273,15 @@ __device__ __forceinline__ float row_sum(float t) {
 }
 
 // PS > 0 (INT codes of PS bits): besides storing the row, write
-// S = -2^(K-24) * (sum of the row's columns) per quantization group (GPT
-// per tile) to sx[(tile * GPT + group) * NSUB*16 + row], then scale the
-// columns by 2^(K - p) for the field pattern (dword v of a lane's 16 bytes
-// holds the two columns of register v), K = kx[pass] (the row's x exponent,
-// uniform over the wave; 0 for the already normalised h).  Lane l holds
-// columns 8l..8l+7 of the 4-tile row, so the 16 lanes of a DPP row are one
-// tile.
+// S = -2^-24 * (sum of the row's columns) per quantization group (GPT per
+// tile) to sx[(tile * GPT + group) * NSUB*16 + row], then pre-scale the
+// columns for the field pattern (dword v of a lane's 16 bytes holds the two
+// columns of register v).  Lane l holds columns 8l..8l+7 of the 4-tile row,
+// so the 16 lanes of a DPP row are one tile.  The staged rows are
+// normalised (x~ = x 2^K, or h~; largest magnitude in [2^6, 2^7)), so the
+// pre-scale makes a value subnormal only below 2^-21 of its row's largest.
 template <int NSUB, int NW, int PS, int GPT>
-__device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t *xs, float *sx, const int *kx,
-                                            int c) {
+__device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t *xs, float *sx, int c) {
   (void)c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -289,17 +289,14 @@ __device__ __forceinline__ void stage_store(const XStage<NSUB, NW> &st, uint16_t
     const int row = NW * p + wave;
     u32x4 v = st.v[p];
     if constexpr (PS > 0) {
-      const int K = kx[p];
       float t = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) t = __builtin_amdgcn_fdot2(as_h2(v[w]), f16x2{1.0f16, 1.0f16}, t, false);
       constexpr int L = 16 / GPT;
       t = row_sum<L>(t);
-      if ((lane & (L - 1)) == 0) sx[(lane / L) * (NSUB * 16) + row] = t * -__builtin_ldexpf(1.0f, K - 24);
+      if ((lane & (L - 1)) == 0) sx[(lane / L) * (NSUB * 16) + row] = t * -0x1p-24f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v[w] = as_u32(as_h2(v[w]) * as_h2(f16x2_pow2(K - int_pattern<PS>(w))));
-    } else {
-      (void)kx;
+      for (int w = 0; w < 4; ++w) v[w] = prescale_pair<PS>(v[w], w);
     }
     *reinterpret_cast<u32x4 *>(xs + row * kXStride + 8 * lane) = v;
   }
@@ -339,7 +336,7 @@ __device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, 
 // z of the chunk's pairs in LDS: sums the ks fp32 partials of the
 // projection kernel (all loads issued before any add) and rounds to fp16;
 // with xk the sum is first scaled by 2^K of the row's token (z of the
-// normalised x~ = x 2^K).
+// normalised x~ = x 2^K; xexp holds K per sorted position).
 // zs layout: [NSUB*16 rows][width] fp16 with width = nset * RZ (RZ padded
 // columns per block); src column base = col0 within each partial row.
 template <int NSUB, int NW>
@@ -350,7 +347,7 @@ __device__ __forceinline__ void z_prologue(const FfnArgs &a, bool xk, const floa
   for (int o = tid; o < n4; o += NW * 64) {
     const int row = (4 * o) / width, col = (4 * o) % width;
     const int m = std::min(row, ch.cnt - 1);
-    const int K = xk ? row_kx(a, ch, m) : 0;
+    const int K = xk ? a.xexp[ch.base + m] : 0;
     const float *src = zpart + (int64_t)(ch.base + m) * zstride + col;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     int k = 0;
@@ -403,9 +400,12 @@ __device__ __forceinline__ void z_preload(const float *zpart, int zstride, int w
   }
 }
 
+// z_store scales row r by 2^kx[r] (kx: the rows' x exponents in LDS).
 template <int NSUB, int NW, int NV>
-__device__ __forceinline__ void z_store(const FfnArgs &a, const Chunk &ch, const ZPre<NSUB, NW, NV> &zp, int width,
-                                       uint16_t *zs) {
+__device__ __forceinline__ void z_store(const FfnArgs &a, const Chunk &ch, const int *kx, const ZPre<NSUB, NW, NV> &zp,
+                                       int width, uint16_t *zs) {
+  (void)a;
+  (void)ch;
   const int tid = threadIdx.x;
   const int n4 = NSUB * 16 * width / 4;
 #pragma unroll
@@ -413,7 +413,7 @@ __device__ __forceinline__ void z_store(const FfnArgs &a, const Chunk &ch, const
     const int o = tid + i * NW * 64;
     if (o < n4) {
       const int row = (4 * o) / width, col = (4 * o) % width;
-      const int K = row_kx(a, ch, row);
+      const int K = kx[row];
       u32x2 h;
       h[0] = as_u32(f16x2{(f16)__builtin_ldexpf(zp.v[i][0], K), (f16)__builtin_ldexpf(zp.v[i][1], K)});
       h[1] = as_u32(f16x2{(f16)__builtin_ldexpf(zp.v[i][2], K), (f16)__builtin_ldexpf(zp.v[i][3], K)});
@@ -460,8 +460,8 @@ struct Stager {
       lut_load<B1>(d1, s1, g4, n_kt, c, l1);
     }
   }
-  __device__ __forceinline__ void store(uint16_t *xs, float *sx, uint16_t *lut_lds, const int *kx, int c) {
-    stage_store<NSUB, NW, PLANE ? 0 : B0, GPT>(st, xs, sx, kx, c);
+  __device__ __forceinline__ void store(uint16_t *xs, float *sx, uint16_t *lut_lds, int c) {
+    stage_store<NSUB, NW, PLANE ? 0 : B0, GPT>(st, xs, sx, c);
     if constexpr (PLANE) {
       lut_store<B0>(l0, lut_lds, c);
       lut_store<B1>(l1, lut_lds + kLutBlk, c);
@@ -488,8 +488,7 @@ __device__ __forceinline__ void compute_two(const Group<B0, PLANE> &g0, const Gr
 // before its prologue, so they arrive during it.
 template <int NSUB, int NW, int GPT, bool PLANE, int B0, int B1>
 __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc &d1, int s0, int s1,
-                                           int g_begin, int g_end, const uint16_t *const *rowp, const int *kx,
-                                           uint16_t *xs,
+                                           int g_begin, int g_end, const uint16_t *const *rowp, uint16_t *xs,
                                            float *sx, uint16_t *lut_lds, f32x4 (*acc)[NSUB],
                                            const Group<B0, PLANE> &m0, const Group<B1, PLANE> &m1) {
   const int n_kt = d0.K / kTileK;
@@ -504,7 +503,7 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
   {
     const int c = std::min(4, n_kt - 4 * g_begin);
     stg.load(d0, d1, rowp, s0, s1, g_begin, n_kt, c);
-    stg.store(xb(g_begin), sb(g_begin), lut_lds, kx, c);
+    stg.store(xb(g_begin), sb(g_begin), lut_lds, c);
     __syncthreads();
   }
   // one full group: the next group's activations load, this group is
@@ -520,7 +519,7 @@ __device__ __forceinline__ void stream_two(const BlockDesc &d0, const BlockDesc 
     compute_two<NSUB, B0, B1, PLANE, 4, GPT>(c0, c1, xb(g), sb(g), lut_lds, acc);
     if (more) {
       if constexpr (NXB == 1) __syncthreads();
-      stg.store(xb(g + 1), sb(g + 1), lut_lds, kx, cn);
+      stg.store(xb(g + 1), sb(g + 1), lut_lds, cn);
       __syncthreads();
     }
   };
@@ -570,24 +569,17 @@ __device__ __forceinline__ void preload_two(const BlockDesc &d0, const BlockDesc
 }
 
 // Wave-uniform row pointers of the staged activations: pass p loads chunk
-// row NW*p + wave (clamped to the last valid row): the token's x row and
-// its exponent (gate/up), or the pair's normalised h row and 0 (down).
+// row NW*p + wave (clamped to the last valid row): the token's normalised
+// x~ row (gate/up) or the pair's normalised h row (down).
 template <int NSUB, int NW>
-__device__ __forceinline__ void row_ptrs(const uint16_t **rowp, int *kx, const FfnArgs &a, const Chunk &ch,
-                                         bool gather) {
+__device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a, const Chunk &ch, bool gather) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int p = 0; p < XStage<NSUB, NW>::NP; ++p) {
     const int m = std::min(NW * p + wave, ch.cnt - 1);
     const uint16_t *ptr;
-    if (gather) {
-      const int t = a.sorted_pairs[ch.base + m] / a.k;
-      ptr = a.x + (int64_t)t * a.H;
-      kx[p] = __builtin_amdgcn_readfirstlane(a.xexp[t]);
-    } else {
-      ptr = a.hn + (int64_t)(ch.base + m) * a.I;
-      kx[p] = 0;
-    }
+    if (gather) ptr = a.xn + (int64_t)(a.sorted_pairs[ch.base + m] / a.k) * a.H;
+    else ptr = a.hn + (int64_t)(ch.base + m) * a.I;
     const uint64_t u = reinterpret_cast<uint64_t>(ptr);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
@@ -597,9 +589,8 @@ __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, int *kx, const F
 
 // LDS layout of both stream kernels: [x staging | z rows (2 RZ columns) |
 // per-group column sums (4 tiles x 2 groups x NSUB*16 rows, fp32) | per wave:
-// its two streams' bit-plane LUTs (bit-plane kernels only) | epilogue:
-// per-wave row maxima of |h| (4 x NSUB*16 fp32) and the rows' x exponents
-// (NSUB*16 int32)].
+// its two streams' bit-plane LUTs (bit-plane kernels only)].  The gate/up
+// epilogue reuses the staging area for its fp32 h tile.
 template <int NSUB, bool PLANE>
 __device__ __forceinline__ int zs_offset() { return xs_bufs<NSUB, PLANE>() * xs_halves<NSUB>(); }
 
@@ -614,40 +605,34 @@ __device__ __forceinline__ uint16_t *lut_region(uint16_t *lds, int RZ, int wave)
                                      xs_bufs<NSUB, PLANE>() * sx_floats<NSUB>()) + wave * 2 * kLutBlk;
 }
 
-template <int NSUB, bool PLANE>
-__device__ __forceinline__ float *epi_region(uint16_t *lds, int RZ) {
-  return reinterpret_cast<float *>(lut_region<NSUB, PLANE>(lds, RZ, PLANE ? 4 : 0));
-}
 
 // gate/up: 4 waves, each streams the gate and the up rows of one 16-row
-// strip; h = SiLU(gate) * up is formed in registers.  INT codes work on the
-// normalised x~ = x 2^K (the staging applies 2^K), bit-plane codes on x
-// (their accumulators are scaled by 2^K before the low-rank terms, whose
-// z rows hold V x~).  h is stored as fp16 h 2^(kNormTop - eb) with eb the
-// exponent of the pair's largest |h| over the workgroup's 64 rows (block
-// sg of I), and eb goes to hblk.
+// strip; h = SiLU(gate) * up is formed in registers.  The kernels work on
+// the normalised x~ = x 2^K (one K per token), so the accumulators and the
+// z rows (V x~) share its units; the epilogue returns to x's in fp32.  h is
+// stored as fp16 h 2^(kNormTop - eb) with eb the exponent of the pair's
+// largest |h| over the workgroup's 64 rows (block sg of I), and eb (int8)
+// goes to hblk.
 template <int NSUB, int GPT, bool PLANE, int BG, int BU>
 __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, int strip, uint16_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t *xs = lds;
   uint16_t *zs = lds + zs_offset<NSUB, PLANE>();
-  float *s_hmax = epi_region<NSUB, PLANE>(lds, a.RZ);
-  int *s_kx = reinterpret_cast<int *>(s_hmax + 4 * NSUB * 16);
   const int zw = 2 * a.RZ;
   const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];   // scalar loads
   Group<BG, PLANE> p0;
   Group<BU, PLANE> p1;
   preload_two<GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, p0, p1);
-  // the rows' x exponents for the epilogue (published by the first staging barrier)
-  if (threadIdx.x < NSUB * 16) s_kx[threadIdx.x] = row_kx(a, ch, threadIdx.x);
+  // the rows' x exponents: requested now, kept in one register and put in
+  // LDS after the K walk (the epilogue reads them there)
+  const int kreg = threadIdx.x < NSUB * 16 ? a.xexp[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
   if (a.comp_on) {
     z_prologue<NSUB, 4>(a, true, a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
-  int kx[XStage<NSUB, 4>::NP];
-  row_ptrs<NSUB, 4>(rowp, kx, a, ch, true);
+  row_ptrs<NSUB, 4>(rowp, a, ch, true);
   const int row = strip * 16 + (lane & 15);
   // first U operands (gate, up), requested before the K walk
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
@@ -661,22 +646,12 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_g4 = (a.H / kTileK + 3) / 4;
-  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, kx, xs,
-                                          sx_region<NSUB, PLANE>(lds, a.RZ),
+  stream_two<NSUB, 4, GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, n_g4, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
                                           lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
-  // units of acc: x~ for INT codes; x for bit-plane codes unless compensated
-  const bool xt = !PLANE || a.comp_on;
+  // (the column sums' LDS is free once every wave has passed the barrier
+  // below; the exponents go there)
+  int *s_kx = reinterpret_cast<int *>(sx_region<NSUB, PLANE>(lds, a.RZ));
   if (a.comp_on) {
-    if constexpr (PLANE) {
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int K = s_kx[16 * s + 4 * (lane >> 4) + i];
-          acc[0][s][i] = __builtin_ldexpf(acc[0][s][i], K);
-          acc[1][s][i] = __builtin_ldexpf(acc[1][s][i], K);
-        }
-    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const BlockDesc &d = b ? du : dg;
@@ -684,34 +659,44 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
       if (a.rs > 0) lowrank_epi<NSUB>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[b]);
     }
   }
-  float hv[NSUB][4];
+  // h = SiLU(gate) * up (back in x's units) in fp32 into LDS [rows][64
+  // columns] (the staging buffers are free once every wave has finished
+  // its K walk), then coalesced: 8 threads (a DPP half-row) per token row
+  // take its largest |h| over the workgroup's 64 columns for eb, and store
+  // h 2^(kNormTop - eb) as fp16
+  float *h32 = reinterpret_cast<float *>(lds);
+  __syncthreads();
+  if (threadIdx.x < NSUB * 16) s_kx[threadIdx.x] = kreg;
+  __syncthreads();
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * s + 4 * (lane >> 4) + i;
-      const int K = xt ? -s_kx[m] : 0;
+      const int K = -s_kx[m];
       const float g = __builtin_ldexpf(acc[0][s][i], K), u = __builtin_ldexpf(acc[1][s][i], K);
-      hv[s][i] = g / (1.0f + __expf(-g)) * u;
-      const float mx = dpp_row_max(__builtin_fabsf(hv[s][i]));
-      if ((lane & 15) == 0) s_hmax[wave * NSUB * 16 + m] = mx;
+      h32[m * kH32Stream + 16 * wave + (lane & 15)] = g / (1.0f + __expf(-g)) * u;
     }
   }
   __syncthreads();
-  const int nb = a.I / 64, sg = strip >> 2;
+  const int tid = threadIdx.x, sg = strip >> 2;
+  if (tid < NSUB * 16 * 8) {
+    const int m = tid >> 3, c8 = 8 * (tid & 7);
+    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(h32 + m * kH32Stream + c8);
+    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(h32 + m * kH32Stream + c8 + 4);
+    float mx = 0.f;
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
+    for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(v0[j]), __builtin_fabsf(v1[j])));
+    const int eb = h_block_exp(dpp_half_row_max(mx));
+    if (m < ch.cnt) {
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * s + 4 * (lane >> 4) + i;
-      const float mx = std::max(std::max(s_hmax[m], s_hmax[NSUB * 16 + m]),
-                                std::max(s_hmax[2 * NSUB * 16 + m], s_hmax[3 * NSUB * 16 + m]));
-      const int eb = ilogb_f32(mx);
-      if (m < ch.cnt) {
-        a.h[(int64_t)(ch.base + m) * a.I + row] =
-            __builtin_bit_cast(uint16_t, (f16)__builtin_ldexpf(hv[s][i], kNormTop - eb));
-        if (wave == 0 && (lane & 15) == 0) a.hblk[(int64_t)(ch.base + m) * nb + sg] = eb;
+      for (int j = 0; j < 2; ++j) {
+        o[j] = as_u32(f16x2{(f16)__builtin_ldexpf(v0[2 * j], kNormTop - eb), (f16)__builtin_ldexpf(v0[2 * j + 1], kNormTop - eb)});
+        o[2 + j] = as_u32(f16x2{(f16)__builtin_ldexpf(v1[2 * j], kNormTop - eb), (f16)__builtin_ldexpf(v1[2 * j + 1], kNormTop - eb)});
       }
+      *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + m) * a.I + 64 * sg + c8) = o;
+      if ((tid & 7) == 0) a.hblk[(int64_t)(ch.base + m) * a.hblk_stride + sg] = (int8_t)eb;
     }
   }
 }
@@ -738,8 +723,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
     __syncthreads();
   }
   const uint16_t *rowp[XStage<NSUB, 4>::NP];
-  int kx[XStage<NSUB, 4>::NP];
-  row_ptrs<NSUB, 4>(rowp, kx, a, ch, false);
+  row_ptrs<NSUB, 4>(rowp, a, ch, false);
   // first U operands of the two strips, requested before the K walk
   f16x8 ub[2] = {pack_b(0, 0, 0, 0), pack_b(0, 0, 0, 0)};
   if (epi && a.r > 0) {
@@ -752,7 +736,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[b][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (g1 > g0)
-    stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, kx, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
+    stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
                                             lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
@@ -787,7 +771,7 @@ __device__ __forceinline__ int chunk_class(int nsub_max) { return nsub_max == 1 
 inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
   const size_t nb = plane ? 1 : (nsub == 1 ? xs_bufs<1, false>() : 1);
   return nb * nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 2 * RZ * 2 + nb * 8 * nsub * 16 * 4 +
-         (plane ? (size_t)4 * 2 * kLutBlk * 2 : 0) + (size_t)5 * nsub * 16 * 4;
+         (plane ? (size_t)4 * 2 * kLutBlk * 2 : 0);
 }
 
 // gate/up: 256 threads; grid.x = max_chunks * (I / 64)

@@ -24,7 +24,7 @@
 namespace moeq {
 
 constexpr int kTM = kTiledM;           // tokens per token tile
-constexpr int kTS = kTileK + 8;        // LDS row stride (halves) of the staged h tile
+constexpr int kH32S = kTileK + 4;      // LDS row stride (floats) of the staged fp32 h tile
 constexpr int kTiledWaves = 4;   // waves per workgroup (8 token tiles x 4 strips each)
 
 // Packed codes and metadata of one strip for one 128-column tile.
@@ -261,8 +261,9 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
     rowoff[i] = (uint32_t)(a.sorted_pairs[ch.base + m] / a.k) * (uint32_t)a.H;
   }
-  // the rows' x exponents, past the LDS stages (published by the K loop's barriers)
-  if (threadIdx.x < kTM) reinterpret_cast<int *>(lds + kTiledLdsBytes)[threadIdx.x] = row_kx(a, ch, threadIdx.x);
+  // the rows' x exponents: requested now, stored past the LDS stages after
+  // the K walk (so that nothing waits for them)
+  const int kreg = threadIdx.x < kTM ? a.xexp[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
   f32x4 acc[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -275,7 +276,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
                                wave,
                                rowoff,
                                lds,
-                               make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * 2u),
+                               make_rsrc(a.xn, (uint32_t)a.T * (uint32_t)a.H * 2u),
                                make_rsrc(dg.codes, code_region_bytes(dg)),
                                make_rsrc(du.codes, code_region_bytes(du))};
   // the low-rank epilogue's inputs (z rows for up to 64 columns from one
@@ -291,21 +292,14 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     ub[q] = a.comp_on && a.r > 0 ? lowrank_bop((q >> 1) ? du.U : dg.U, a.r, strips[q] * 16 + (lane & 15), 0)
                                  : pack_b(0, 0, 0, 0);
   kl.template run<8>(acc);
-  // acc holds W x; with compensation it is moved to the units of the
-  // normalised x~ = x 2^K before the low-rank terms (z rows hold V x~)
-  const int *s_kx = reinterpret_cast<const int *>(lds + kTiledLdsBytes);
+  // acc holds W x~ (x~ = x 2^K, the normalised rows), as do the z rows
+  int *s_kx = reinterpret_cast<int *>(lds + kTiledLdsBytes);
+  if (threadIdx.x < kTM) s_kx[threadIdx.x] = kreg;
+  __syncthreads();
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int K = s_kx[16 * s + 4 * (lane >> 4) + i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q][s][i] = __builtin_ldexpf(acc[q][s][i], K);
-      }
     uint16_t *zs = l16;
-    if (zpre) z_store<8, 4, 8>(a, ch, zp, zw, zs);
+    if (zpre) z_store<8, 4, 8>(a, ch, s_kx, zp, zw, zs);
     else z_prologue<8, 4>(a, true, a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
 #pragma unroll
@@ -318,55 +312,46 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     }
     __syncthreads();
   }
-  // h = SiLU(gate) * up, then per token the largest |h| over the
-  // workgroup's 128 columns (lanes of a DPP row, then the 4 waves)
-  float *s_hmax = reinterpret_cast<float *>(lds + kTM * kTS * 2);     // [4][128], past the h tile
+  // h = SiLU(gate) * up (gate and up back in x's units) in fp32 into LDS
+  // [128 tokens][128 columns]
+  float *h32 = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * s + 4 * (lane >> 4) + i;
-      const int K = a.comp_on ? -s_kx[m] : 0;
-      float mx = 0.f;
+      const int K = -s_kx[m];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const float gv = __builtin_ldexpf(acc[g][s][i], K), uv = __builtin_ldexpf(acc[2 + g][s][i], K);
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        acc[g][s][i] = hv;
-        mx = std::max(mx, __builtin_fabsf(hv));
+        h32[m * kH32S + 32 * wave + 16 * g + (lane & 15)] = gv / (1.0f + __expf(-gv)) * uv;
       }
-      mx = dpp_row_max(mx);
-      if ((lane & 15) == 0) s_hmax[wave * kTM + m] = mx;
     }
   }
   __syncthreads();
-  // h 2^(kNormTop - eb) into LDS [128 tokens][128 columns], then coalesced rows
-  uint16_t *hs = l16;
-  const int nb = a.I / 64;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * s + 4 * (lane >> 4) + i;
-      const float mx = std::max(std::max(s_hmax[m], s_hmax[kTM + m]), std::max(s_hmax[2 * kTM + m], s_hmax[3 * kTM + m]));
-      const int eb = ilogb_f32(mx);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int col = 32 * wave + 16 * g + (lane & 15);
-        hs[m * kTS + col] = __builtin_bit_cast(uint16_t, (f16)__builtin_ldexpf(acc[g][s][i], kNormTop - eb));
-      }
-      if (wave == 0 && (lane & 15) < 2 && m < ch.cnt)
-        a.hblk[(int64_t)(ch.base + m) * nb + 2 * nt + (lane & 15)] = eb;
-    }
-  }
-  __syncthreads();
+  // coalesced rows, 16 threads (one DPP row) per token: the row's largest
+  // |h| gives eb, then h 2^(kNormTop - eb) as fp16; eb goes to hblk for both
+  // 64-column halves of this 128-column block
   const int tid = threadIdx.x, c8 = 8 * (tid & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = (tid >> 4) + 16 * i;
-    if (r < ch.cnt)
-      *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + r) * a.I + nt * kTileK + c8) =
-          *reinterpret_cast<const u32x4 *>(hs + r * kTS + c8);
+    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(h32 + r * kH32S + c8);
+    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(h32 + r * kH32S + c8 + 4);
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(v0[j]), __builtin_fabsf(v1[j])));
+    const int eb = h_block_exp(dpp_row_max(mx));
+    if (r < ch.cnt) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        o[j] = as_u32(f16x2{(f16)__builtin_ldexpf(v0[2 * j], kNormTop - eb), (f16)__builtin_ldexpf(v0[2 * j + 1], kNormTop - eb)});
+        o[2 + j] = as_u32(f16x2{(f16)__builtin_ldexpf(v1[2 * j], kNormTop - eb), (f16)__builtin_ldexpf(v1[2 * j + 1], kNormTop - eb)});
+      }
+      *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + r) * a.I + nt * kTileK + c8) = o;
+      if ((tid & 15) < 2) a.hblk[(int64_t)(ch.base + r) * a.hblk_stride + 2 * nt + (tid & 15)] = (int8_t)eb;
+    }
   }
 }
 
