@@ -90,10 +90,18 @@ def build_layers(cfg, seed, copies, formats):
             W = torch.from_numpy(gen.gen_weight_block(cfg, seed, e, blk)).cuda()
             for name, c in formats.items():
                 blocks[name].append(moeq.quantize_block(W, c["fmt"], int(bits_of[name][e, blk]), c["G"]))
-            del W
-            if cfg["r"]:
+            if cfg["r"] and cfg.get("comp") == "svd":
+                # rank-r truncation of the RTN residual, fitted on the device
+                # (the first format's quantization; INT layers only)
+                q = blocks[next(iter(formats))][-1]
+                r = cfg["r"]
+                l = min(r + 16, 128, *W.shape)
+                omega = torch.from_numpy(gen.gen_test_matrix(cfg, seed, e, blk, l)).cuda()
+                factors.append(moeq.fit_lowrank(W, q["codes"], q["scales"], q["zeros"], cfg["G"], omega, r, 2))
+            elif cfg["r"]:
                 f = gen.gen_factors(cfg, seed, e, blk)
                 factors.append((torch.from_numpy(f[0]).cuda(), torch.from_numpy(f[1]).cuda()))
+            del W
     shared = None
     if cfg.get("rs"):
         shared = []
@@ -523,9 +531,14 @@ def main():
         ent = tr.get(cfg["name"], {})
         if ent.get("source_hash") == kernel_source_hash():
             traffic = ent.get("kernels", {}).get("gateup_stream", {}).get("bytes")
+    # the dominant kernel (gate/up) by the bench contract, and beside it the
+    # whole step (route + every FFN kernel) against the same peak
+    step_gbs = alg["bytes"] / (ms * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=(achieved / HBM_PEAK_GBS) if achieved else None, traffic=traffic,
-                    kernel="gateup_stream", bytes_per_launch=alg["gateup_bytes"])
+                    kernel="gateup_stream", bytes_per_launch=alg["gateup_bytes"],
+                    whole_step=dict(achieved=step_gbs, frac=step_gbs / HBM_PEAK_GBS, bytes=alg["bytes"],
+                                    what="algorithmic bytes of the layer / step time (route + expert FFN)"))
     ffn_us = sum(v["avg_us"] for n, v in kern.items() if n != "route")
     out = {
         "metric": METRIC,

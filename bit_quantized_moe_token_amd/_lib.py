@@ -63,6 +63,12 @@ SIGNATURES = [
     ("moeq_committed_bits", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     ("moeq_plane_region", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(c_void_p),
                                   ctypes.POINTER(c_size_t)]),
+    ("moeq_plane_release", c_i32, [c_void_p, c_i32, c_i32, c_void_p, c_size_t, c_void_p]),
+    ("moeq_plane_reload", c_i32, [c_void_p, c_i32, c_i32, c_i32, c_void_p, c_size_t, c_void_p]),
+    ("moeq_plane_event", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_void_p)]),
+    ("moeq_resident_planes", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_i32)]),
+    ("moeq_set_desired_bits", c_i32, [c_void_p, c_i32, c_i32, c_i32]),
+    ("moeq_desired_bits", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     ("moeq_route_workspace_size", c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_size_t)]),
     ("moeq_route", c_i32, [c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing), c_void_p, c_size_t, c_void_p]),
     ("moeq_plan_reductions", c_i32, [c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double),

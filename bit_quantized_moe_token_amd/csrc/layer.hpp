@@ -60,7 +60,19 @@ struct moeq_layer {
   size_t bytes;
   moeq::BlockDesc *d_desc;                 // device table (inside buf)
   std::vector<moeq::BlockDesc> h_desc;     // host copy of the table
-  std::vector<uint8_t> bits;               // [E*3]
+  std::vector<uint8_t> bits;               // [E*3] committed q (b for INT)
   std::vector<size_t> block_alg_bytes;     // [E*3]
   std::vector<size_t> shared_alg_bytes;    // [groups*3]
+  // bit-plane page table: planes [0, resident) of a block are in device
+  // memory; desired is the bitwidth the runtime is moving the block to.
+  // commit_ev is recorded after each commit of the block, copy_ev after
+  // each release or reload; reload_pending marks a reload no commit has
+  // waited for yet.  (Host-side state, enqueue order; events exist for
+  // bit-plane layers only.)
+  std::vector<uint8_t> resident, desired, reload_pending;   // [E*3]
+  std::vector<hipEvent_t> commit_ev, copy_ev;                // [E*3]
+  ~moeq_layer() {
+    for (hipEvent_t e : commit_ev) (void)hipEventDestroy(e);
+    for (hipEvent_t e : copy_ev) (void)hipEventDestroy(e);
+  }
 };

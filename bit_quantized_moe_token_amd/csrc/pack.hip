@@ -362,6 +362,20 @@ MOEQ_API moeq_status moeq_pack(const moeq_layer_desc *d, void *device_buf, size_
     delete L;
     return fail(MOEQ_ERR_HIP, "pack: descriptor copy failed: %s", hipGetErrorString(hipGetLastError()));
   }
+  L->resident.assign(nb, d->fmt == MOEQ_FMT_BITPLANE ? 4 : 0);
+  L->desired.assign(d->bits, d->bits + nb);
+  L->reload_pending.assign(nb, 0);
+  if (d->fmt == MOEQ_FMT_BITPLANE) {
+    L->commit_ev.reserve(nb);
+    L->copy_ev.reserve(nb);
+    for (int b = 0; b < nb; ++b) {
+      hipEvent_t e0, e1;
+      if (hipEventCreateWithFlags(&e0, hipEventDisableTiming) != hipSuccess) { delete L; return fail(MOEQ_ERR_HIP, "pack: event creation failed"); }
+      L->commit_ev.push_back(e0);
+      if (hipEventCreateWithFlags(&e1, hipEventDisableTiming) != hipSuccess) { delete L; return fail(MOEQ_ERR_HIP, "pack: event creation failed"); }
+      L->copy_ev.push_back(e1);
+    }
+  }
   *out = L;
   return MOEQ_OK;
 }
@@ -427,8 +441,17 @@ MOEQ_API moeq_status moeq_commit_bits(moeq_layer *L, int32_t e, int32_t blk, int
   if (q < 2 || q > 4) return fail(MOEQ_ERR_INVALID, "commit_bits: q=%d not in {2,3,4}", q);
   if (!lut) return fail(MOEQ_ERR_INVALID, "commit_bits: null LUT");
   const int b = 3 * e + blk;
+  if (q > L->resident[b])
+    return fail(MOEQ_ERR_INVALID, "commit_bits: q=%d needs planes %d..%d of block (%d,%d), which are released "
+                "(reload them with moeq_plane_reload first)", q, L->resident[b], q - 1, e, blk);
   BlockDesc &bd = L->h_desc[b];
   const int n_kt = bd.K / kTileK;
+  // a reload of this block's planes lands before the new bitwidth is used
+  if (L->reload_pending[b]) {
+    if (hipStreamWaitEvent(stream, L->copy_ev[b], 0) != hipSuccess)
+      return fail(MOEQ_ERR_HIP, "commit_bits: stream wait failed: %s", hipGetErrorString(hipGetLastError()));
+    L->reload_pending[b] = 0;
+  }
   prof_begin("commit_bits", stream);
   hipLaunchKernelGGL(pack_lut_kernel, dim3(nblocks((int64_t)bd.N * n_kt << q)), dim3(256), 0, stream,
                      lut, bd.N, bd.K, q, const_cast<uint16_t *>(bd.lut));
@@ -436,6 +459,9 @@ MOEQ_API moeq_status moeq_commit_bits(moeq_layer *L, int32_t e, int32_t blk, int
   prof_end("commit_bits", stream);
   moeq_status st = check_launch("commit_bits");
   if (st != MOEQ_OK) return st;
+  // releases of this block wait for everything enqueued up to here
+  if (hipEventRecord(L->commit_ev[b], stream) != hipSuccess)
+    return fail(MOEQ_ERR_HIP, "commit_bits: event record failed: %s", hipGetErrorString(hipGetLastError()));
   const size_t nk = (size_t)bd.N * bd.K;
   const size_t old_codes = nk * bd.bits / 8 + (nk / kTileK) * ((size_t)2 << bd.bits);
   const size_t new_codes = nk * q / 8 + (nk / kTileK) * ((size_t)2 << q);
@@ -461,5 +487,101 @@ MOEQ_API moeq_status moeq_plane_region(const moeq_layer *L, int32_t e, int32_t b
   const BlockDesc &bd = L->h_desc[3 * e + blk];
   *ptr = const_cast<uint8_t *>(bd.codes) + (size_t)plane * bd.plane_bytes;
   *bytes = bd.plane_bytes;
+  return MOEQ_OK;
+}
+
+// ---- page movement ([PW] "What carries the argument" and Figure 4: a
+// lowered bitwidth is committed before its pages are released; released
+// pages come back before a higher bitwidth is committed).
+
+static moeq_status plane_block(const moeq_layer *L, int32_t e, int32_t blk, const char *what, int *b) {
+  if (!L) return fail(MOEQ_ERR_INVALID, "%s: null layer", what);
+  if (e < 0 || e >= L->dims.E || blk < 0 || blk > 2) return fail(MOEQ_ERR_INVALID, "%s: bad block (%d,%d)", what, e, blk);
+  if (L->dims.fmt != MOEQ_FMT_BITPLANE) return fail(MOEQ_ERR_UNSUPPORTED, "%s: not a bit-plane layer", what);
+  *b = 3 * e + blk;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_resident_planes(const moeq_layer *L, int32_t e, int32_t blk, int32_t *n) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "resident_planes", &b);
+  if (st != MOEQ_OK) return st;
+  if (!n) return fail(MOEQ_ERR_INVALID, "resident_planes: null output");
+  *n = L->resident[b];
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_set_desired_bits(moeq_layer *L, int32_t e, int32_t blk, int32_t d) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "set_desired_bits", &b);
+  if (st != MOEQ_OK) return st;
+  if (d < 2 || d > 4) return fail(MOEQ_ERR_INVALID, "set_desired_bits: d=%d not in {2,3,4}", d);
+  L->desired[b] = (uint8_t)d;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_desired_bits(const moeq_layer *L, int32_t e, int32_t blk, int32_t *d) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "desired_bits", &b);
+  if (st != MOEQ_OK) return st;
+  if (!d) return fail(MOEQ_ERR_INVALID, "desired_bits: null output");
+  *d = L->desired[b];
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_plane_release(moeq_layer *L, int32_t e, int32_t blk, void *host, size_t host_bytes,
+                                        hipStream_t stream) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "plane_release", &b);
+  if (st != MOEQ_OK) return st;
+  const BlockDesc &bd = L->h_desc[b];
+  const int q = bd.bits, res = L->resident[b];
+  if (q >= res) return MOEQ_OK;                        // nothing above the committed bitwidth
+  const size_t pb = bd.plane_bytes;
+  if (!host) return fail(MOEQ_ERR_INVALID, "plane_release: null host buffer");
+  if (host_bytes < (size_t)res * pb)
+    return fail(MOEQ_ERR_INVALID, "plane_release: host buffer has %zu bytes, planes up to %d need %zu", host_bytes,
+                res - 1, (size_t)res * pb);
+  // after every kernel enqueued before the block's last commit
+  if (hipStreamWaitEvent(stream, L->commit_ev[b], 0) != hipSuccess ||
+      hipMemcpyAsync(static_cast<uint8_t *>(host) + (size_t)q * pb, bd.codes + (size_t)q * pb, (size_t)(res - q) * pb,
+                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipEventRecord(L->copy_ev[b], stream) != hipSuccess)
+    return fail(MOEQ_ERR_HIP, "plane_release: %s", hipGetErrorString(hipGetLastError()));
+  L->resident[b] = (uint8_t)q;
+  L->reload_pending[b] = 0;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_plane_reload(moeq_layer *L, int32_t e, int32_t blk, int32_t q, const void *host,
+                                       size_t host_bytes, hipStream_t stream) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "plane_reload", &b);
+  if (st != MOEQ_OK) return st;
+  if (q < 2 || q > 4) return fail(MOEQ_ERR_INVALID, "plane_reload: q=%d not in {2,3,4}", q);
+  const int res = L->resident[b];
+  if (q <= res) return MOEQ_OK;                         // already resident
+  const BlockDesc &bd = L->h_desc[b];
+  const size_t pb = bd.plane_bytes;
+  if (!host) return fail(MOEQ_ERR_INVALID, "plane_reload: null host buffer");
+  if (host_bytes < (size_t)q * pb)
+    return fail(MOEQ_ERR_INVALID, "plane_reload: host buffer has %zu bytes, planes up to %d need %zu", host_bytes, q - 1,
+                (size_t)q * pb);
+  if (hipMemcpyAsync(const_cast<uint8_t *>(bd.codes) + (size_t)res * pb,
+                     static_cast<const uint8_t *>(host) + (size_t)res * pb, (size_t)(q - res) * pb,
+                     hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(L->copy_ev[b], stream) != hipSuccess)
+    return fail(MOEQ_ERR_HIP, "plane_reload: %s", hipGetErrorString(hipGetLastError()));
+  L->resident[b] = (uint8_t)q;
+  L->reload_pending[b] = 1;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_plane_event(const moeq_layer *L, int32_t e, int32_t blk, hipEvent_t *ev) {
+  int b;
+  moeq_status st = plane_block(L, e, blk, "plane_event", &b);
+  if (st != MOEQ_OK) return st;
+  if (!ev) return fail(MOEQ_ERR_INVALID, "plane_event: null output");
+  *ev = L->copy_ev[b];
   return MOEQ_OK;
 }

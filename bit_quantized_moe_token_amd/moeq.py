@@ -189,6 +189,38 @@ class PackedLayer:
         check(lib().moeq_committed_bits(self.handle, e, blk, ctypes.byref(q)), "moeq_committed_bits")
         return q.value
 
+    def plane_release(self, e, blk, host, stream=None):
+        """Copy the planes above the committed q to the pinned host tensor
+        `host` (uint8, plane p at offset p * plane_bytes) on `stream`
+        (default: the current stream) and mark them released."""
+        s = ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+        check(lib().moeq_plane_release(self.handle, e, blk, _ptr(host), host.numel(), s), "moeq_plane_release")
+
+    def plane_reload(self, e, blk, q, host, stream=None):
+        """Copy planes back from `host` until q planes are resident (see
+        moeq_plane_reload)."""
+        s = ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+        check(lib().moeq_plane_reload(self.handle, e, blk, q, _ptr(host), host.numel(), s), "moeq_plane_reload")
+
+    def plane_event(self, e, blk):
+        """The hipEvent_t (as an integer) of the block's last release or reload copy."""
+        ev = c_void_p(0)
+        check(lib().moeq_plane_event(self.handle, e, blk, ctypes.byref(ev)), "moeq_plane_event")
+        return ev.value
+
+    def resident_planes(self, e, blk):
+        n = ctypes.c_int32(0)
+        check(lib().moeq_resident_planes(self.handle, e, blk, ctypes.byref(n)), "moeq_resident_planes")
+        return n.value
+
+    def set_desired_bits(self, e, blk, d):
+        check(lib().moeq_set_desired_bits(self.handle, e, blk, d), "moeq_set_desired_bits")
+
+    def desired_bits(self, e, blk):
+        d = ctypes.c_int32(0)
+        check(lib().moeq_desired_bits(self.handle, e, blk, ctypes.byref(d)), "moeq_desired_bits")
+        return d.value
+
     def plane_region(self, e, blk, plane):
         """(device address, bytes) of bit-plane `plane` (0 = most significant)."""
         ptr, n = c_void_p(0), ctypes.c_size_t(0)

@@ -244,6 +244,54 @@ moeq_status moeq_debug_unpack(const moeq_layer *L, int32_t e, int32_t blk,
  */
 moeq_status moeq_commit_bits(moeq_layer *L, int32_t expert, int32_t block, int32_t q,
                              const uint16_t *lut, hipStream_t stream);
+
+/*
+ * Page movement of bit-plane blocks ([PW] "What carries the argument" and
+ * the Figure 4 caption: at the offload threshold the lowered bitwidth is
+ * committed and the pages above it are released to host memory; at the
+ * reload threshold the pages come back before the higher bitwidth is
+ * committed).  Every block keeps, host side, its committed q, the number of
+ * its planes resident in device memory (4 after packing; planes are
+ * released from the least significant one down) and a desired bitwidth d
+ * (set by the caller's policy, e.g. from moeq_plan_reductions; d starts at
+ * the packed q).  Nothing here allocates memory or synchronises the host.
+ *
+ * moeq_plane_release — copy the block's planes above its committed q to
+ * host memory and mark them released.  The copy is enqueued on `stream`
+ * after all work enqueued before the block's last moeq_commit_bits (the
+ * kernels that may still read those planes).  Once the copy has completed
+ * (work enqueued later on `stream`, or anything waiting on the event of
+ * moeq_plane_event), the caller may reuse the released device bytes
+ * (moeq_plane_region) until it reloads them.  A block with no plane above
+ * its committed q is left as it is.
+ *   host HOST [host_bytes], pinned, caller-owned; plane p is written at
+ *   offset p * plane_bytes, for planes q .. resident - 1; host_bytes must
+ *   cover the planes up to resident - 1.
+ *
+ * moeq_plane_reload — copy planes resident .. q-1 of the block back from
+ * host memory (same layout) on `stream` and mark planes 0 .. q-1 resident.
+ * The caller must have stopped using the reused bytes before the copy (in
+ * `stream` order).  The next moeq_commit_bits of the block makes its own
+ * stream wait for this copy, so a commit to q never runs ahead of its
+ * planes.  q in {2, 3, 4}; a q at or below the resident count does nothing.
+ *
+ * moeq_commit_bits returns MOEQ_ERR_INVALID for a q above the resident
+ * count (its planes must be reloaded first).
+ *
+ * moeq_plane_event — the event recorded after the block's last release or
+ * reload copy (owned by the layer; valid until moeq_layer_destroy).
+ * moeq_resident_planes, moeq_set_desired_bits, moeq_desired_bits — the
+ * page-table state (d in {2, 3, 4}).  Bit-plane layers only
+ * (MOEQ_ERR_UNSUPPORTED for INT layers).
+ */
+moeq_status moeq_plane_release(moeq_layer *L, int32_t expert, int32_t block, void *host,
+                               size_t host_bytes, hipStream_t stream);
+moeq_status moeq_plane_reload(moeq_layer *L, int32_t expert, int32_t block, int32_t q,
+                              const void *host, size_t host_bytes, hipStream_t stream);
+moeq_status moeq_plane_event(const moeq_layer *L, int32_t expert, int32_t block, hipEvent_t *ev);
+moeq_status moeq_resident_planes(const moeq_layer *L, int32_t expert, int32_t block, int32_t *n);
+moeq_status moeq_set_desired_bits(moeq_layer *L, int32_t expert, int32_t block, int32_t d);
+moeq_status moeq_desired_bits(const moeq_layer *L, int32_t expert, int32_t block, int32_t *d);
 moeq_status moeq_committed_bits(const moeq_layer *L, int32_t expert, int32_t block, int32_t *q);
 moeq_status moeq_plane_region(const moeq_layer *L, int32_t expert, int32_t block, int32_t plane,
                               void **ptr, size_t *bytes);

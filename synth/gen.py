@@ -11,6 +11,7 @@ key, so that changing T (or drawing fewer rows) never shifts any other draw:
   [seed, 5]                      Zipf permutation of experts (router bias)
   [seed, 6]                      outlier activation channels
   [seed, 7, grp, blk, 0|1]       shared compensator factors U | V, N(0, 0.01)
+  [seed, 8, e, blk]              Gaussian test matrix of the compensator fit, N(0, 1)
 
 "N(0, s)" is read as mean 0 and standard deviation s.  Two optional config
 keys move a layer across the fp16 range without changing any draw: x_scale
@@ -160,6 +161,13 @@ def gen_shared_factors(cfg, seed, grp, blk):
     U = (_rng(seed, 7, grp, blk, 0).standard_normal((n, rs)) * 0.01).astype(np.float16)
     V = (_rng(seed, 7, grp, blk, 1).standard_normal((rs, kdim)) * 0.01).astype(np.float16)
     return U, V
+
+
+def gen_test_matrix(cfg, seed, e, blk, l):
+    """Gaussian test matrix [K, l] fp32 of the randomized compensator fit of
+    block (e, blk) (K = the block's input dimension)."""
+    _, kdim = block_shape(cfg, blk)
+    return _rng(seed, 8, e, blk).standard_normal((kdim, l)).astype(np.float32)
 
 
 def n_groups(cfg):

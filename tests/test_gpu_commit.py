@@ -111,3 +111,78 @@ def test_commit_rejections(setup):
     with pytest.raises(moeq.MoeqError):
         int_layer.commit_bits(0, 0, 3, torch.zeros((tiny["I"], tiny["H"] // tiny["G"], 16),
                                                    dtype=torch.float16, device="cuda"))
+
+
+def test_release_reload_cycle(setup):
+    """Page movement through the library: lower eight experts' blocks to
+    q = 2 and release their two low planes to pinned host memory on a side
+    stream, reuse (overwrite) the freed device bytes there, reload, and
+    commit q = 4 on the compute stream with no host synchronisation in
+    between (the commit waits for the reload itself).  The output matches
+    the oracle at every step, and committing the packed bitwidths back
+    restores the first output bit for bit."""
+    from bit_quantized_moe_token_amd import moeq
+    dev, x, logits = setup
+    E, n_comp = CFG["E"], CFG["n_comp"]
+    bits0 = gen.gen_bits(CFG, 0)
+    y0 = _run(dev, x, logits, n_comp)
+    blocks = [(e, b) for e in range(8) for b in range(3)]
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    luts = {(e, b, q): _lut(e, b, q) for e, b in blocks for q in (2, 4)}
+    torch.cuda.synchronize()
+    host = {}
+    base = dev.buf.data_ptr()
+    for e, b in blocks:
+        assert dev.resident_planes(e, b) == 4
+        dev.set_desired_bits(e, b, 2)
+        assert dev.desired_bits(e, b) == 2
+        dev.commit_bits(e, b, 2, luts[(e, b, 2)])                   # lower first ...
+        ptr, pb = dev.plane_region(e, b, 0)
+        host[(e, b)] = torch.empty(4 * pb, dtype=torch.uint8, pin_memory=True)
+        dev.plane_release(e, b, host[(e, b)], stream=side)           # ... then release
+        assert dev.resident_planes(e, b) == 2
+        with torch.cuda.stream(side):                                # reuse the freed bytes
+            p2, _ = dev.plane_region(e, b, 2)
+            dev.buf[p2 - base:p2 - base + 2 * pb].fill_(0xA5)
+    with pytest.raises(moeq.MoeqError):                              # planes 2, 3 are gone
+        dev.commit_bits(0, 0, 4, luts[(0, 0, 4)])
+    bits2 = bits0.copy()
+    for e, b in blocks:
+        bits2[e, b] = 2
+    y2 = _run(dev, x, logits, n_comp)
+    orc2 = layers.oracle_layer(CFG, 0, cache_blocks=3 * E, bits=bits2)
+    layers.check_y(y2.cpu().numpy(), layers.oracle_y(orc2, CFG, x, logits, n_comp), "released planes")
+    for e, b in blocks:                                              # reload, then raise
+        dev.set_desired_bits(e, b, 4)
+        dev.plane_reload(e, b, 4, host[(e, b)], stream=side)
+        assert dev.resident_planes(e, b) == 4
+        dev.commit_bits(e, b, 4, luts[(e, b, 4)])                    # on `main`, after the reload
+    assert torch.cuda.current_stream() == main
+    bits4 = bits0.copy()
+    for e, b in blocks:
+        bits4[e, b] = 4
+    y4 = _run(dev, x, logits, n_comp)
+    orc4 = layers.oracle_layer(CFG, 0, cache_blocks=3 * E, bits=bits4)
+    layers.check_y(y4.cpu().numpy(), layers.oracle_y(orc4, CFG, x, logits, n_comp), "reloaded planes")
+    for e, b in blocks:
+        dev.commit_bits(e, b, int(bits0[e, b]), _lut(e, b, int(bits0[e, b])))
+    assert torch.equal(_run(dev, x, logits, n_comp), y0)
+
+
+def test_page_movement_rejections(setup):
+    from bit_quantized_moe_token_amd import moeq
+    dev, x, logits = setup
+    small = torch.empty(16, dtype=torch.uint8, pin_memory=True)
+    dev.commit_bits(1, 1, 2, _lut(1, 1, 2))
+    with pytest.raises(moeq.MoeqError):                              # host buffer too small
+        dev.plane_release(1, 1, small)
+    with pytest.raises(moeq.MoeqError):
+        dev.set_desired_bits(1, 1, 5)
+    with pytest.raises(moeq.MoeqError):
+        dev.plane_reload(1, 1, 1, small)
+    dev.commit_bits(1, 1, int(gen.gen_bits(CFG, 0)[1, 1]), _lut(1, 1, int(gen.gen_bits(CFG, 0)[1, 1])))
+    tiny = configs.get("tiny")
+    int_layer = layers.device_layer(tiny, 0, layers.oracle_layer(tiny, 0))
+    with pytest.raises(moeq.MoeqError):
+        int_layer.resident_planes(0, 0)

@@ -58,16 +58,17 @@ def _run(dev, cfg, x, logits, n_comp, out_dtype=torch.float16, split_k=0, path=P
     return y
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("case", list(CASES))
-def test_ffn_matches_oracle(case):
-    cfg, orc, dev, x, logits = _setup(case)
+def test_ffn_matches_oracle(case, seed):
+    cfg, orc, dev, x, logits = _setup(case, seed)
     y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
     rel, fro = layers.check_y(y.cpu().numpy(), ref, case)
-    print(f"{case}: max|err|/rms {rel:.2e}  fro {fro:.2e}")
+    print(f"{case} seed {seed}: max|err|/rms {rel:.2e}  fro {fro:.2e}")
     # fp16 output stays inside the same bound
     y16 = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float16)
-    layers.check_y(y16.float().cpu().numpy(), ref, case + " fp16")
+    layers.check_y(y16.float().cpu().numpy(), ref, f"{case} seed {seed} fp16")
 
 
 @pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane"])

@@ -1,9 +1,11 @@
-"""GPU parity at the full Mixtral-shaped sizes (H 4096, I 14336, 8 experts,
-top-2) in the launch configuration the benchmark times: the whole layer is
-quantized and packed by the library, routed and evaluated for the whole
-batch, and the oracle recomputes sampled outputs one by one (every gate/up
-row of the sampled tokens' experts, the down rows of the sampled output
-columns) from its own quantization of the same fp16 weights."""
+"""GPU parity at full size in the launch configuration the benchmark times:
+the Mixtral-shaped layers (H 4096, I 14336, 8 experts, top-2) and the
+bit-plane layer with shared factors (128 experts, top-8, 512 tokens, all
+4096 pairs routed).  The whole layer is quantized and packed by the
+library, routed and evaluated for the whole batch, and the oracle
+recomputes sampled outputs one by one (every gate/up row of the sampled
+tokens' experts, the down rows of the sampled output columns) from its own
+quantization of the same fp16 weights."""
 
 import numpy as np
 import pytest
@@ -56,3 +58,13 @@ def test_prefill_full_size_sampled():
     T = configs.get("prefill")["T"]
     tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 7).astype(int)]))
     _run_full("prefill", tokens, 256)
+
+
+@pytest.mark.timeout(600)
+def test_bitplane_full_size_sampled():
+    """Bit-plane layer: 128 experts, top-8, 512 tokens (4096 pairs), q per
+    block in {2, 3, 4}, shared rank-32 factors per 4 experts plus rank-8
+    per expert; tokens sampled across the batch."""
+    T = configs.get("bitplane")["T"]
+    tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 6).astype(int)]))
+    _run_full("bitplane", tokens, 256)
