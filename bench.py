@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the routed low-bit MoE expert layer on one MI355X.
 
-One step = one pass of the hot path over one batch: moeq_route (top-k +
-counting sort) followed by moeq_expert_ffn (V-projections, gate/up + SwiGLU,
-down, combine) on a seeded synthetic layer.  Default workload: the
+One step = one pass of the hot path over one batch: routing (top-k +
+counting sort) and the expert FFN (V-projections, gate/up + SwiGLU, down,
+combine) on a seeded synthetic layer, through moeq_moe_forward (which runs
+the gate/up projection beside the routing for decode batches); --no-fused
+times moeq_route followed by moeq_expert_ffn.  Default workload: the
 Mixtral-shaped decode layer (8 experts, top-2, H 4096, I 14336, 16 tokens,
 int3 group-128 codes, rank-32 compensators).  Inputs are resident in HBM
 before timing; weights rotate over several packed copies so that no step
@@ -68,6 +70,8 @@ def parse():
                    help="skip the tiny, fine-grained and bit-plane layers (keep the prefill one)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph instead of launching it directly")
+    p.add_argument("--no-fused", action="store_true",
+                   help="time moeq_route followed by moeq_expert_ffn instead of moeq_moe_forward")
     return p.parse_args()
 
 
@@ -198,7 +202,7 @@ def step_distribution(fn, steps):
     return dict(median=statistics.median(ts), p10=q(0.1), p90=q(0.9), n=len(ts))
 
 
-def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, graph=False, split_k=0):
+def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, graph=False, split_k=0, fused=True):
     import numpy as np
     import torch
     from bit_quantized_moe_token_amd import moeq
@@ -209,12 +213,16 @@ def run_workload(cfg, layers_list, seed, steps, warmup, path, profile=True, grap
     logits = torch.from_numpy(gen.gen_logits(cfg, seed)).cuda()
     rt = moeq.RoutingOut(T, cfg["E"], k, x.device)
     y = torch.empty((T, cfg["H"]), dtype=torch.float16, device=x.device)
-    ws = moeq.FfnWorkspace(layers_list[0], T, k, path, split_k)
+    ws = moeq.FfnWorkspace(layers_list[0], T, k, path, split_k, forward=fused)
     R = len(layers_list)
 
     def step(i):
-        moeq.route(logits, k, out=rt)
-        moeq.expert_ffn(layers_list[i % R], x, rt, cfg["n_comp"], out=y, ws=ws, path=path, split_k=split_k)
+        # one pass of the hot path: routing and the expert layer
+        if fused:
+            moeq.moe_forward(layers_list[i % R], logits, x, k, cfg["n_comp"], routing=rt, out=y, ws=ws)
+        else:
+            moeq.route(logits, k, out=rt)
+            moeq.expert_ffn(layers_list[i % R], x, rt, cfg["n_comp"], out=y, ws=ws, path=path, split_k=split_k)
 
     timed = step
     if graph:
@@ -518,7 +526,7 @@ def main():
         copy_calibration()
 
     ms, prof, alg = run_workload(cfg, layers["main"], args.seed, args.steps, args.warmup, args.path,
-                                 graph=args.graph, split_k=args.split_k)
+                                 graph=args.graph, split_k=args.split_k, fused=not args.no_fused)
     T = cfg["T"]
     tokens_s = T / (ms * 1e-3)
 
@@ -569,7 +577,8 @@ def main():
     }
     if extra_cfg is not None:
         pms, pprof, palg = run_workload(extra_cfg, layers["prefill"], args.seed, max(10, args.steps // 10),
-                                        max(5, args.warmup // 4), args.path, graph=args.graph)
+                                        max(5, args.warmup // 4), args.path, graph=args.graph,
+                                        fused=not args.no_fused)
         pk = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in pprof.items()}
         out["prefill"] = dict(workload=extra_cfg["name"], ms_per_step=pms,
                               tokens_s=extra_cfg["T"] / (pms * 1e-3), alg_flops=palg["flops"],
@@ -586,7 +595,8 @@ def main():
             ocfg = configs.get(short)
             olayers = build_layers(ocfg, args.seed, {"main": R}, {"main": ocfg})["main"]
             oms, oprof, oalg = run_workload(ocfg, olayers, args.seed, max(20, args.steps // 4),
-                                            max(5, args.warmup // 4), args.path, graph=args.graph)
+                                            max(5, args.warmup // 4), args.path, graph=args.graph,
+                                            fused=not args.no_fused)
             ok = {n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in oprof.items()}
             out["other_configs"][short] = dict(
                 workload=ocfg["name"], ms_per_step=oms, tokens_s=ocfg["T"] / (oms * 1e-3),

@@ -81,6 +81,10 @@ SIGNATURES = [
     ("moeq_ffn_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions), ctypes.POINTER(c_size_t)]),
     ("moeq_expert_ffn", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
                                 c_void_p, c_i32, c_void_p, c_size_t, ctypes.POINTER(FfnOptions), c_void_p]),
+    ("moeq_forward_workspace_size", c_i32, [c_void_p, c_i32, c_i32, ctypes.POINTER(FfnOptions),
+                                            ctypes.POINTER(c_size_t)]),
+    ("moeq_moe_forward", c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32, ctypes.POINTER(Routing),
+                                 c_void_p, c_i32, c_void_p, c_size_t, ctypes.POINTER(FfnOptions), c_void_p]),
     ("moeq_ffn_noalloc_max_bytes", c_i32, [ctypes.POINTER(c_size_t)]),
     ("moeq_expert_ffn_noalloc", c_i32, [c_void_p, c_void_p, c_i32, c_i32, ctypes.POINTER(Routing), c_i32,
                                         c_void_p, c_i32, ctypes.POINTER(FfnOptions), c_void_p]),

@@ -6,6 +6,7 @@
 //   (split-K partials) -> gate-weighted combine (undoes the h exponent)
 #include "common.hpp"
 #include "ffn.hpp"
+#include "route.hpp"
 #include "layer.hpp"
 
 namespace moeq {
@@ -68,25 +69,151 @@ static int pick_ks(int P, int K) {
 
 static int hblk_stride(const moeq_layer *L) { return (L->dims.I / 64 + 15) / 16 * 16; }
 
-static Ws ws_plan(const moeq_layer *L, int T, int k, int splits) {
+// z_tok: the gate/up projection covers every (token, expert) pair (the
+// fused routing path) instead of the routed pairs.
+static Ws ws_plan(const moeq_layer *L, int T, int k, int splits, bool z_tok = false) {
   const int64_t P = (int64_t)T * k;
+  const int64_t PZ = z_tok ? (int64_t)T * L->dims.E : P;
   const int Rp = (L->dims.r + 31) / 32 * 32, Rsp = (L->dims.rs + 31) / 32 * 32;
   const int RZ = Rp + Rsp;
   Ws w;
-  w.ks_gu = pick_ks((int)P, L->dims.H);
+  w.ks_gu = pick_ks((int)PZ, L->dims.H);
   w.ks_d = pick_ks((int)P, L->dims.I);
   size_t off = 0;
-  w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * P * 2 * RZ * 4);
+  w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * PZ * 2 * RZ * 4);
   w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
   w.h = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.hblk = off; off = al256(off + (size_t)P * hblk_stride(L));
   w.hn = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.hexp = off; off = al256(off + (size_t)P * 4);
-  w.xexp = off; off = al256(off + (size_t)P * 4);
+  w.xexp = off; off = al256(off + (size_t)T * 4);
   w.xn = off; off = al256(off + (size_t)T * L->dims.H * 2);
   w.ypart = off; off = al256(off + (size_t)splits * P * L->dims.H * 4);
   w.total = off;
   return w;
+}
+
+// Argument checks, workspace layout and the argument block of one call.
+static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, int32_t k, const moeq_routing *r,
+                             int32_t n_comp, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
+                             const moeq_ffn_options *opts, bool z_tok, FfnArgs *out, int *path_out) {
+  if (!L || !r) return fail(MOEQ_ERR_INVALID, "expert_ffn: null layer or routing");
+  const LayerDims &D = L->dims;
+  if (T < 0 || k < 1 || k > D.E) return fail(MOEQ_ERR_INVALID, "expert_ffn: T=%d k=%d invalid for E=%d", T, k, D.E);
+  if (n_comp < 0 || n_comp > k) return fail(MOEQ_ERR_INVALID, "expert_ffn: n_comp=%d not in 0..%d", n_comp, k);
+  if (y_dtype != MOEQ_F16 && y_dtype != MOEQ_F32) return fail(MOEQ_ERR_INVALID, "expert_ffn: bad y_dtype %d", y_dtype);
+  const int path = pick_path(L, T, k, opts);
+  if (path < 0)
+    return fail(MOEQ_ERR_UNSUPPORTED, "expert_ffn: path %d not available for this layer and batch",
+                opts ? opts->path : 0);
+  if (opts && (opts->split_k < 0 || opts->split_k > 64)) return fail(MOEQ_ERR_INVALID, "expert_ffn: split_k=%d not in 0..64", opts->split_k);
+  *path_out = path;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !y || !r->topk_gates || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
+    return fail(MOEQ_ERR_INVALID, "expert_ffn: null pointer");
+  const int splits = pick_splits(L, T, k, opts);
+  const Ws w = ws_plan(L, T, k, splits, z_tok);
+  if (!ws || ws_bytes < w.total)
+    return fail(MOEQ_ERR_WORKSPACE, "expert_ffn: workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+
+  uint8_t *wb = static_cast<uint8_t *>(ws);
+  FfnArgs &a = *out;
+  a.desc = L->d_desc;
+  a.offsets = r->expert_offsets;
+  a.sorted_pairs = r->sorted_pairs;
+  a.x = x;
+  a.gates = r->topk_gates;
+  a.pair_pos = r->pair_pos;
+  a.E = D.E; a.H = D.H; a.I = D.I; a.k = k; a.T = T; a.n_comp = n_comp;
+  a.r = D.r; a.rs = D.rs;
+  a.Rp = (D.r + 31) / 32 * 32; a.Rsp = (D.rs + 31) / 32 * 32; a.RZ = a.Rp + a.Rsp;
+  a.comp_on = (n_comp > 0 && a.RZ > 0) ? 1 : 0;
+  a.zp_gu = reinterpret_cast<float *>(wb + w.zp_gu);
+  a.zp_d = reinterpret_cast<float *>(wb + w.zp_d);
+  a.z_tok = z_tok ? 1 : 0;
+  a.ks_gu = w.ks_gu;
+  a.ks_d = w.ks_d;
+  a.ks_stride_gu = (int64_t)T * (z_tok ? D.E : k) * 2 * a.RZ;
+  a.ks_stride_d = (int64_t)T * k * a.RZ;
+  a.h = reinterpret_cast<uint16_t *>(wb + w.h);
+  a.hblk = reinterpret_cast<int8_t *>(wb + w.hblk);
+  a.hblk_stride = hblk_stride(L);
+  a.hn = reinterpret_cast<uint16_t *>(wb + w.hn);
+  a.hexp = reinterpret_cast<int32_t *>(wb + w.hexp);
+  a.xexp = reinterpret_cast<int32_t *>(wb + w.xexp);
+  a.xn = reinterpret_cast<uint16_t *>(wb + w.xn);
+  a.ypart = reinterpret_cast<float *>(wb + w.ypart);
+  a.splits = splits;
+  a.P = T * k;
+  a.G = D.G;
+  a.fmt = D.fmt;
+  a.nsub_max = std::max(1, std::min(kMT, T) / 16 + (std::min(kMT, T) % 16 ? 1 : 0));
+  return MOEQ_OK;
+}
+
+// First launch: x exponents and the normalised x * 2^K that the gate/up
+// kernels read, with the gate/up projection when there is one (of the
+// routed pairs, or with z_tok of every (token, expert) pair).
+static void ffn_front(const FfnArgs &a, hipStream_t stream) {
+  if (a.comp_on) {
+    prof_begin("lowrank_project_gu", stream);
+    if (a.z_tok)
+      launch_lowrank_project(a, 2, dim3((a.T + 15) / 16 * a.E, 2 * a.RZ / 16), stream);
+    else
+      launch_lowrank_project(a, 0, dim3(max_chunks(a.E, a.T, a.k) * kSubPerChunk, 2 * a.RZ / 16), stream);
+    prof_end("lowrank_project_gu", stream);
+  } else {
+    prof_begin("xexp", stream);
+    launch_xexp(a, stream);
+    prof_end("xexp", stream);
+  }
+}
+
+// The rest of the call, after routing and ffn_front.
+static moeq_status ffn_rest(const FfnArgs &a, int path, void *y, int32_t y_dtype, hipStream_t stream) {
+  const int mc = max_chunks(a.E, a.T, a.k);
+  const bool tiled = path == MOEQ_PATH_TILED;
+  const int mt = tiled ? max_chunks(a.E, a.T, a.k, kTiledM) : 0;     // token tiles of the tiled path
+  if (tiled) {
+    prof_begin("gateup_tiled", stream);
+    launch_tiled_gateup(a, (mt * (a.I / kTileK) + 7) / 8 * 8, stream);
+    prof_end("gateup_tiled", stream);
+  } else {
+    prof_begin("gateup_stream", stream);
+    launch_gateup_stream(a, mc * (a.I / 64), stream);
+    prof_end("gateup_stream", stream);
+  }
+  // h renormalised to one exponent per pair (with the down projection when
+  // there is one)
+  if (a.comp_on) {
+    prof_begin("lowrank_project_down", stream);
+    launch_lowrank_project(a, 1, dim3(mc * kSubPerChunk, a.RZ / 16), stream);
+    prof_end("lowrank_project_down", stream);
+  } else {
+    prof_begin("hnorm", stream);
+    launch_hnorm(a, stream);
+    prof_end("hnorm", stream);
+  }
+  if (tiled) {
+    prof_begin("down_tiled", stream);
+    launch_tiled_down(a, (mt * (a.H / 256) + 7) / 8 * 8, stream);
+    prof_end("down_tiled", stream);
+  } else {
+    prof_begin("down_stream", stream);
+    launch_down_stream(a, mc * (a.H / 128) * a.splits, stream);
+    prof_end("down_stream", stream);
+  }
+  prof_begin("combine", stream);
+  launch_combine(a, y, y_dtype == MOEQ_F32, stream);
+  prof_end("combine", stream);
+  return check_launch("expert_ffn");
+}
+
+// The fused routing path serves decode-sized batches whose expert count is
+// small against k (the projection of every (token, expert) pair then costs
+// little more than that of the routed pairs) on the weight-streaming path.
+static bool fusable(const moeq_layer *L, int T, int k, const moeq_ffn_options *opts) {
+  return T >= 1 && T <= kRouteTokens && L->dims.E <= kMaxE && L->dims.E <= 4 * k && pick_path(L, T, k, opts) == MOEQ_PATH_STREAM;
 }
 
 }  // namespace moeq
@@ -106,101 +233,41 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
                                      const moeq_routing *r, int32_t n_comp, void *y, int32_t y_dtype,
                                      void *ws, size_t ws_bytes, const moeq_ffn_options *opts,
                                      hipStream_t stream) {
-  if (!L || !r) return fail(MOEQ_ERR_INVALID, "expert_ffn: null layer or routing");
-  const LayerDims &D = L->dims;
-  if (T < 0 || k < 1 || k > D.E) return fail(MOEQ_ERR_INVALID, "expert_ffn: T=%d k=%d invalid for E=%d", T, k, D.E);
-  if (n_comp < 0 || n_comp > k) return fail(MOEQ_ERR_INVALID, "expert_ffn: n_comp=%d not in 0..%d", n_comp, k);
-  if (y_dtype != MOEQ_F16 && y_dtype != MOEQ_F32) return fail(MOEQ_ERR_INVALID, "expert_ffn: bad y_dtype %d", y_dtype);
-  const int path = pick_path(L, T, k, opts);
-  if (path < 0)
-    return fail(MOEQ_ERR_UNSUPPORTED, "expert_ffn: path %d not available for this layer and batch",
-                opts ? opts->path : 0);
-  if (opts && (opts->split_k < 0 || opts->split_k > 64)) return fail(MOEQ_ERR_INVALID, "expert_ffn: split_k=%d not in 0..64", opts->split_k);
-  if (T == 0) return MOEQ_OK;
-  if (!x || !y || !r->topk_gates || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
-    return fail(MOEQ_ERR_INVALID, "expert_ffn: null pointer");
-  const int splits = pick_splits(L, T, k, opts);
-  const bool tiled = path == MOEQ_PATH_TILED;
-  const Ws w = ws_plan(L, T, k, splits);
-  if (!ws || ws_bytes < w.total)
-    return fail(MOEQ_ERR_WORKSPACE, "expert_ffn: workspace has %zu bytes, needs %zu", ws_bytes, w.total);
-
-  uint8_t *wb = static_cast<uint8_t *>(ws);
   FfnArgs a;
-  a.desc = L->d_desc;
-  a.offsets = r->expert_offsets;
-  a.sorted_pairs = r->sorted_pairs;
-  a.x = x;
-  a.gates = r->topk_gates;
-  a.pair_pos = r->pair_pos;
-  a.E = D.E; a.H = D.H; a.I = D.I; a.k = k; a.T = T; a.n_comp = n_comp;
-  a.r = D.r; a.rs = D.rs;
-  a.Rp = (D.r + 31) / 32 * 32; a.Rsp = (D.rs + 31) / 32 * 32; a.RZ = a.Rp + a.Rsp;
-  a.comp_on = (n_comp > 0 && a.RZ > 0) ? 1 : 0;
-  a.zp_gu = reinterpret_cast<float *>(wb + w.zp_gu);
-  a.zp_d = reinterpret_cast<float *>(wb + w.zp_d);
-  a.ks_gu = w.ks_gu;
-  a.ks_d = w.ks_d;
-  a.ks_stride_gu = (int64_t)T * k * 2 * a.RZ;
-  a.ks_stride_d = (int64_t)T * k * a.RZ;
-  a.h = reinterpret_cast<uint16_t *>(wb + w.h);
-  a.hblk = reinterpret_cast<int8_t *>(wb + w.hblk);
-  a.hblk_stride = hblk_stride(L);
-  a.hn = reinterpret_cast<uint16_t *>(wb + w.hn);
-  a.hexp = reinterpret_cast<int32_t *>(wb + w.hexp);
-  a.xexp = reinterpret_cast<int32_t *>(wb + w.xexp);
-  a.xn = reinterpret_cast<uint16_t *>(wb + w.xn);
-  a.ypart = reinterpret_cast<float *>(wb + w.ypart);
-  a.splits = splits;
-  a.P = T * k;
+  int path = 0;
+  moeq_status st = ffn_setup(L, x, T, k, r, n_comp, y, y_dtype, ws, ws_bytes, opts, false, &a, &path);
+  if (st != MOEQ_OK || T == 0) return st;
+  ffn_front(a, stream);
+  return ffn_rest(a, path, y, y_dtype, stream);
+}
 
-  const int mc = max_chunks(D.E, T, k);
-  a.G = D.G;
-  a.fmt = D.fmt;
-  a.nsub_max = std::max(1, std::min(kMT, T) / 16 + (std::min(kMT, T) % 16 ? 1 : 0));
-  // x exponents and the normalised x * 2^K that the gate/up kernels read
-  // (with the gate/up projection when there is one)
-  if (a.comp_on) {
-    prof_begin("lowrank_project_gu", stream);
-    launch_lowrank_project(a, 0, dim3(mc * kSubPerChunk, 2 * a.RZ / 16), stream);
-    prof_end("lowrank_project_gu", stream);
-  } else {
-    prof_begin("xexp", stream);
-    launch_xexp(a, stream);
-    prof_end("xexp", stream);
+MOEQ_API moeq_status moeq_forward_workspace_size(const moeq_layer *L, int32_t T, int32_t k,
+                                                 const moeq_ffn_options *opts, size_t *bytes) {
+  moeq_status st = moeq_ffn_workspace_size(L, T, k, opts, bytes);
+  if (st != MOEQ_OK) return st;
+  if (fusable(L, T, k, opts)) *bytes = ws_plan(L, T, k, pick_splits(L, T, k, opts), true).total;
+  return MOEQ_OK;
+}
+
+MOEQ_API moeq_status moeq_moe_forward(const moeq_layer *L, const float *logits, const uint16_t *x, int32_t T,
+                                      int32_t k, int32_t n_comp, const moeq_routing *r, void *y, int32_t y_dtype,
+                                      void *ws, size_t ws_bytes, const moeq_ffn_options *opts, hipStream_t stream) {
+  if (!L || !r) return fail(MOEQ_ERR_INVALID, "moe_forward: null layer or routing");
+  if (!fusable(L, T, k, opts)) {
+    // routing, then the expert FFN (the FFN's workspace is the whole ws)
+    moeq_status st = moeq_route(logits, T, L->dims.E, k, r, nullptr, 0, stream);
+    if (st != MOEQ_OK) return st;
+    return moeq_expert_ffn(L, x, T, k, r, n_comp, y, y_dtype, ws, ws_bytes, opts, stream);
   }
-  const int mt = tiled ? max_chunks(D.E, T, k, kTiledM) : 0;     // token tiles of the tiled path
-  if (tiled) {
-    prof_begin("gateup_tiled", stream);
-    launch_tiled_gateup(a, (mt * (D.I / kTileK) + 7) / 8 * 8, stream);
-    prof_end("gateup_tiled", stream);
-  } else {
-    prof_begin("gateup_stream", stream);
-    launch_gateup_stream(a, mc * (D.I / 64), stream);
-    prof_end("gateup_stream", stream);
-  }
-  // h renormalised to one exponent per pair (with the down projection when
-  // there is one)
-  if (a.comp_on) {
-    prof_begin("lowrank_project_down", stream);
-    launch_lowrank_project(a, 1, dim3(mc * kSubPerChunk, a.RZ / 16), stream);
-    prof_end("lowrank_project_down", stream);
-  } else {
-    prof_begin("hnorm", stream);
-    launch_hnorm(a, stream);
-    prof_end("hnorm", stream);
-  }
-  if (tiled) {
-    prof_begin("down_tiled", stream);
-    launch_tiled_down(a, (mt * (D.H / 256) + 7) / 8 * 8, stream);
-    prof_end("down_tiled", stream);
-  } else {
-    prof_begin("down_stream", stream);
-    launch_down_stream(a, mc * (D.H / 128) * splits, stream);
-    prof_end("down_stream", stream);
-  }
-  prof_begin("combine", stream);
-  launch_combine(a, y, y_dtype == MOEQ_F32, stream);
-  prof_end("combine", stream);
-  return check_launch("expert_ffn");
+  FfnArgs a;
+  int path = 0;
+  moeq_status st = ffn_setup(L, x, T, k, r, n_comp, y, y_dtype, ws, ws_bytes, opts, true, &a, &path);
+  if (st != MOEQ_OK) return st;
+  if (!logits || !r->topk_ids) return fail(MOEQ_ERR_INVALID, "moe_forward: null pointer");
+  // routing, x exponents and every pair's gate/up projection in one launch
+  const RouteOut ro{logits, r->topk_ids, r->topk_gates, r->expert_offsets, r->sorted_pairs, r->pair_pos};
+  prof_begin("front_routed", stream);
+  launch_front_routed(a, ro, stream);
+  prof_end("front_routed", stream);
+  return ffn_rest(a, path, y, y_dtype, stream);
 }

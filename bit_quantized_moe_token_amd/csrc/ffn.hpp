@@ -26,7 +26,9 @@ struct FfnArgs {
   int r, rs, Rp, Rsp, RZ;
   int comp_on;
   int G, fmt;
-  float *zp_gu;     // [ks_gu][P][2][RZ] fp32 partial V x (summed by the consumer)
+  float *zp_gu;     // [ks_gu][P][2][RZ] fp32 partial V x (summed by the consumer), by sorted
+                    // position; with z_tok [ks_gu][T][E][2][RZ] by (token, expert), every pair
+  int z_tok;
   float *zp_d;      // [ks_d][P][RZ] fp32 partial V_down h
   int ks_gu, ks_d;  // K splits of the two projections
   int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
@@ -35,7 +37,7 @@ struct FfnArgs {
   int hblk_stride;  // bytes per row of hblk (I/64 rounded up to 16)
   uint16_t *hn;     // [P][I] fp16: h * 2^(kNormTop - eh), eh = the pair's largest eb
   int32_t *hexp;    // [P] eh
-  int32_t *xexp;    // [P] K of the pair's token, by sorted position (x_norm_exp)
+  int32_t *xexp;    // [T] K of each token (x_norm_exp)
   uint16_t *xn;     // [T][H] x * 2^K, the activations the gate/up kernels read
   float *ypart;     // [splits][P][H] fp32, in units of 2^(eh - kNormTop) (the combine undoes it)
   int splits;
@@ -101,8 +103,7 @@ __device__ __forceinline__ int h_block_exp(float mx) {
 
 // x exponents of tokens t = wid, wid + nw, ...: one wave per token takes
 // the largest |x| of the row (fp16 magnitude bits compare as integers),
-// writes K = x_norm_exp of its exponent to the token's k sorted positions
-// and the row x 2^K to xn.
+// writes K = x_norm_exp of its exponent and the row x 2^K to xn.
 __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   const int lane = threadIdx.x & 63;
   for (int t = wid; t < a.T; t += nw) {
@@ -116,7 +117,7 @@ __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
 #pragma unroll
     for (int o = 32; o; o >>= 1) m = std::max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
     const int K = x_norm_exp(ilogb_f16bits(m));
-    for (int j = lane; j < a.k; j += kWave) a.xexp[a.pair_pos[(int64_t)t * a.k + j]] = K;
+    if (lane == 0) a.xexp[t] = K;
     const uint32_t mul = f16x2_pow2(K);
     uint16_t *out = a.xn + (int64_t)t * a.H;
     for (int c = 8 * lane; c < a.H; c += 8 * kWave)
@@ -148,6 +149,11 @@ __device__ __forceinline__ void pair_eh16(const FfnArgs &a, int pos0, int pos_la
   if ((tid & 15) == 0) s_eh[r] = e;
 }
 
+// x exponent of chunk row m (rows past the count repeat the last one).
+__device__ __forceinline__ int row_kx(const FfnArgs &a, const Chunk &ch, int m) {
+  return a.xexp[a.sorted_pairs[ch.base + std::min(m, ch.cnt - 1)] / a.k];
+}
+
 // Upper bound of the number of chunks of MT pairs for T tokens, top-k, E
 // experts (an expert holds at most T pairs).
 inline int max_chunks(int E, int T, int k, int MT = kMT) {
@@ -158,10 +164,13 @@ inline int max_chunks(int E, int T, int k, int MT = kMT) {
   return (int)std::max<int64_t>(0, std::min(a, b));
 }
 
+struct RouteOut;   // route.hpp
+
 // Launchers (stream.hip, lowrank.hip).
 void launch_gateup_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_down_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s);
+void launch_front_routed(const FfnArgs &a, const RouteOut &ro, hipStream_t s);   // needs a.z_tok, a.T <= kRouteTokens
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s);
 void launch_xexp(const FfnArgs &a, hipStream_t s);    // x exponents alone (no gate/up projection)
 void launch_hnorm(const FfnArgs &a, hipStream_t s);   // h renormalisation alone (no down projection)

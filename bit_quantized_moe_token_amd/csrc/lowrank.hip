@@ -7,6 +7,7 @@
 // y_t = sum_j g_{t,j} y_pair(t, j) summed in slot order.
 #include "common.hpp"
 #include "ffn.hpp"
+#include "route.hpp"
 
 namespace moeq {
 
@@ -17,25 +18,48 @@ namespace moeq {
 // every job, so the activations are read NJ times less often); 4 waves
 // split the range and reduce through LDS in fixed order.
 // grid.x = max_chunks * kSubPerChunk tiles, grid.y = (#blocks) * (Rp + Rsp) / 16 / NJ
-// (+ 1 in mode 0), grid.z = ks.  mode 0: v = x[token] (gate/up blocks);
-// the extra y slice (blockIdx.y == njy) computes the tokens' x exponents
+// (+ 1 in modes 0 and 2), grid.z = ks.  mode 0: v = x[token] (gate/up
+// blocks) of each routed pair; mode 2: the same for every (token, expert)
+// pair (grid.x = ceil(T / 16) * E), which needs no routing; in both the
+// extra y slice (blockIdx.y == njy) computes the tokens' x exponents
 // instead.  mode 1: v = h of the pair, renormalised on the fly from its
 // per-block exponents to the pair's exponent eh; the workgroups of y slice
 // 0 also store that renormalised h (hn) and eh, which the down kernels and
 // the combine read.
-template <int NJ>
-__global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy) {
+// ROUTE (mode 2 only): one more y slice, whose first workgroup routes the
+// tokens (route_block) while the others project; the projection of every
+// (token, expert) pair needs no routing, so both fit in one launch.
+template <int NJ, bool ROUTE>
+__global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy, RouteOut ro) {
   __shared__ f32x4 s_part[4][NJ][64];
   __shared__ int s_eh[16];
   __shared__ __attribute__((aligned(16))) int8_t s_eb[16 * 256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (mode == 0 && (int)blockIdx.y >= njy) {
+  if (mode != 1 && (int)blockIdx.y >= njy) {
+    if constexpr (ROUTE) {
+      if ((int)blockIdx.y > njy) {
+        if (blockIdx.x == 0 && blockIdx.z == 0) {
+          __shared__ RouteLds<4> s_route;
+          route_block<256>(ro, a.T, a.E, a.k, s_route);
+        }
+        return;
+      }
+    }
     xexp_rows(a, ((int)blockIdx.z * (int)gridDim.x + (int)blockIdx.x) * 4 + wave, (int)(gridDim.x * gridDim.z) * 4);
     return;
   }
-  const int chunk = blockIdx.x / kSubPerChunk, sub = blockIdx.x % kSubPerChunk;
+  // mode 2: every (token, expert) pair, tokens in place of sorted positions
+  const bool tok = mode == 2;
   Chunk ch;
-  if (!find_chunk(a.offsets, a.E, chunk, &ch)) return;
+  int sub;
+  if (tok) {
+    ch.e = (int)blockIdx.x % a.E;
+    sub = (int)blockIdx.x / a.E;
+    ch.m0 = 0; ch.base = 0; ch.cnt = a.T;
+  } else {
+    sub = blockIdx.x % kSubPerChunk;
+    if (!find_chunk(a.offsets, a.E, blockIdx.x / kSubPerChunk, &ch)) return;
+  }
   if (16 * sub >= ch.cnt) return;
   // mode 1: eh of the tile's 16 pairs; y slice 0 writes hn and eh
   const bool write_hn = mode == 1 && blockIdx.y == 0;
@@ -47,10 +71,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
       a.hexp[ch.base + 16 * sub + threadIdx.x] = s_eh[threadIdx.x];
   }
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
-  const int K = mode == 0 ? a.H : a.I;
-  const int KS = mode == 0 ? a.ks_gu : a.ks_d;
-  float *zbase = mode == 0 ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
-  const int zstride = mode == 0 ? 2 * a.RZ : a.RZ;
+  const bool gu = mode != 1;
+  const int K = gu ? a.H : a.I;
+  const int KS = gu ? a.ks_gu : a.ks_d;
+  float *zbase = gu ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
+  const int zstride = gu ? 2 * a.RZ : a.RZ;
+  // output row of chunk row m: its sorted position, or (mode 2) token * E + e
+  auto zrow = [&](int m) -> int64_t { return tok ? (int64_t)m * a.E + ch.e : (int64_t)(ch.base + m); };
   int zcol[NJ];
   bool live[NJ], vi[NJ];
   const uint16_t *vrow[NJ];
@@ -61,7 +88,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     const int bi = job / jobs_per_blk, rem = job % jobs_per_blk;
     const int set = rem < a.Rp / 16 ? 0 : 1;
     const int it = set ? rem - a.Rp / 16 : rem;
-    const BlockDesc &d = a.desc[3 * ch.e + (mode == 0 ? bi : 2)];
+    const BlockDesc &d = a.desc[3 * ch.e + (gu ? bi : 2)];
     const uint16_t *V = set ? d.Vs : d.V;
     const int R = set ? a.rs : a.r;
     zcol[j] = bi * a.RZ + set * a.Rp + 16 * it + (lane & 15);
@@ -82,13 +109,14 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
         const int m = 16 * sub + 4 * (lane >> 4) + q;
         if (m < ch.cnt)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) zbase[(int64_t)(ch.base + m) * zstride + zcol[j]] = 0.0f;
+          for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = 0.0f;
       }
     return;
   }
   const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
   const int pos = ch.base + mloc;
-  const uint16_t *arow = (mode == 0) ? a.x + (int64_t)(a.sorted_pairs[pos] / a.k) * a.H
+  const uint16_t *arow = mode == 0 ? a.x + (int64_t)(a.sorted_pairs[pos] / a.k) * a.H
+                         : mode == 2 ? a.x + (int64_t)pos * a.H
                                      : a.h + (int64_t)pos * a.I;
   arow += 8 * (lane >> 4);
   // mode 1: the lane's row of h is renormalised per 64-column block by
@@ -163,11 +191,11 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   for (int q = 0; q < 4; ++q) {
     const int m = 16 * sub + 4 * (lane >> 4) + q;
     if (m < ch.cnt) {
-      const int p2 = ch.base + m;
-      const bool comp = (a.sorted_pairs[p2] % a.k) < a.n_comp;
+      // by sorted position: zero for a pair outside its token's leading
+      // n_comp slots; by token (mode 2) the consumer applies that mask
+      const bool comp = tok || (a.sorted_pairs[ch.base + m] % a.k) < a.n_comp;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        zbase[(int64_t)p2 * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
+      for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
     }
   }
 }
@@ -236,7 +264,7 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 }
 
 void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
-  grid.z = mode == 0 ? a.ks_gu : a.ks_d;
+  grid.z = mode != 1 ? a.ks_gu : a.ks_d;
   // two, four or eight jobs per workgroup when many tokens leave no K
   // split (the activation re-reads dominate; fewer jobs keep enough
   // workgroups); the job count is always even
@@ -246,13 +274,23 @@ void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s
   else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) nj = 2;
   grid.y /= nj;
   const int njy = (int)grid.y;
-  if (mode == 0) grid.y += 1;                 // the x-exponent slice
+  if (mode != 1) grid.y += 1;                 // the x-exponent slice
+  const RouteOut ro{};
   switch (nj) {
-    case 8: hipLaunchKernelGGL(lowrank_project_kernel<8>, grid, dim3(256), 0, s, a, mode, njy); break;
-    case 4: hipLaunchKernelGGL(lowrank_project_kernel<4>, grid, dim3(256), 0, s, a, mode, njy); break;
-    case 2: hipLaunchKernelGGL(lowrank_project_kernel<2>, grid, dim3(256), 0, s, a, mode, njy); break;
-    default: hipLaunchKernelGGL(lowrank_project_kernel<1>, grid, dim3(256), 0, s, a, mode, njy); break;
+    case 8: hipLaunchKernelGGL((lowrank_project_kernel<8, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+    case 4: hipLaunchKernelGGL((lowrank_project_kernel<4, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+    case 2: hipLaunchKernelGGL((lowrank_project_kernel<2, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+    default: hipLaunchKernelGGL((lowrank_project_kernel<1, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
   }
+}
+
+// Routing, x exponents and (with compensation) the gate/up projection of
+// every (token, expert) pair in one launch; up to kRouteTokens tokens.
+// Without compensation there are no projection slices (njy = 0).
+void launch_front_routed(const FfnArgs &a, const RouteOut &ro, hipStream_t s) {
+  const int njy = a.comp_on ? 2 * a.RZ / 16 : 0;
+  const dim3 grid(a.comp_on ? (a.T + 15) / 16 * a.E : (a.T + 3) / 4, njy + 2, a.comp_on ? a.ks_gu : 1);
+  hipLaunchKernelGGL((lowrank_project_kernel<1, true>), grid, dim3(256), 0, s, a, 2, njy, ro);
 }
 
 // x exponents when no gate/up projection runs: one wave per token.

@@ -10,206 +10,18 @@
 // offsets (MxMoE abstract: uneven expert activation makes per-expert work
 // heterogeneous, so experts get contiguous, variable-length row ranges).
 //
-// Phase 1: one wave per token; k rounds of a wave-wide argmax over
-//          (logit desc, expert id asc).
-// Phase 2: LDS histogram -> exclusive scan -> expert_offsets.
-// Phase 3: pairs in chunks of 1024 in ascending pair id; a pair's rank among
-//          equal experts inside its wave comes from ballots over the expert
-//          id bits (peer mask) and mbcnt; across waves and chunks from
-//          per-wave counters in LDS.  Every pair's slot is computed, none is
-//          found by atomics, so the result is deterministic.
-#include "common.hpp"
+// The single-workgroup routing (route_block in route.hpp) runs one wave
+// per token; ties in the top-k order go to the lower expert id.
+#include "route.hpp"
 
 namespace moeq {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kMaxE = 256;
-constexpr int kRouteTokens = 16;   // most tokens of the single-workgroup kernel: one per wave
-
-struct Cand {
-  float v;
-  int id;
-};
-
-__device__ __forceinline__ Cand better(Cand a, Cand b) {
-  return (a.v > b.v || (a.v == b.v && a.id < b.id)) ? a : b;
-}
-
-// c against its partner lane under one DPP lane permutation (ctrl: a DPP
-// control constant; every lane of a row is a valid source).
-template <int CTRL>
-__device__ __forceinline__ Cand dpp_better(Cand c) {
-  Cand o;
-  o.v = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, c.v), CTRL, 0xf, 0xf, true));
-  o.id = __builtin_amdgcn_mov_dpp(c.id, CTRL, 0xf, 0xf, true);
-  return better(c, o);
-}
-
-// Wave-wide best candidate, the same in every lane.  `better` is a total
-// order on (value desc, id asc), so the result does not depend on the
-// reduction tree: within each 16-lane row by DPP exchanges (quad swaps,
-// then half-row and row mirrors: every lane ends with its row's best),
-// then across the four rows through their first lanes.
-__device__ __forceinline__ Cand wave_argmax(Cand c) {
-  c = dpp_better<0xb1>(c);    // quad_perm [1,0,3,2]
-  c = dpp_better<0x4e>(c);    // quad_perm [2,3,0,1]
-  c = dpp_better<0x141>(c);   // row_half_mirror
-  c = dpp_better<0x140>(c);   // row_mirror
-  Cand r[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    r[q].v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 16 * q));
-    r[q].id = __builtin_amdgcn_readlane(c.id, 16 * q);
-  }
-  return better(better(r[0], r[1]), better(r[2], r[3]));
-}
-
-constexpr int kSlots = kMaxE / kWave;   // logits (and selected slots) per lane
-
-// Logits of token t: lane l holds experts l + 64 s.
-__device__ __forceinline__ void load_logits(const float *__restrict__ logits, int t, int E, float *v) {
-  const int lane = threadIdx.x & 63;
-  const float *row = logits + (int64_t)t * E;
-#pragma unroll
-  for (int s = 0; s < kSlots; ++s) {
-    const int e = lane + s * kWave;
-    v[s] = e < E ? row[e] : 0.0f;
-  }
-}
-
-// Top-k of token t by one wave from its logits v: k rounds of a wave-wide
-// argmax, gates in fp32.  The selected ids and logits stay in registers
-// (slot j with lane j % 64) until all rounds are done, so no round waits
-// for memory; then lanes j < k write slot j (and, if given, count it in
-// the LDS histogram and copy its id to LDS).
-__device__ __forceinline__ void topk_token(const float *v, int t, int E, int k, int32_t *__restrict__ ids,
-                                           float *__restrict__ gates, int *s_hist, int *s_ids) {
-  const int lane = threadIdx.x & 63;
-  uint32_t taken = 0;
-  float top0 = 0.0f, denom = 0.0f;
-  float sel[kSlots];   // logit of slot j kept by lane j % 64
-  int sid[kSlots];     // its expert id
-#pragma unroll
-  for (int s = 0; s < kSlots; ++s) { sel[s] = 0.0f; sid[s] = 0; }
-  for (int j = 0; j < k; ++j) {
-    Cand c{-__builtin_inff(), 0x7fffffff};
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const int e = lane + s * kWave;
-      if (e < E && !((taken >> s) & 1u)) c = better(c, Cand{v[s], e});
-    }
-    c = wave_argmax(c);                       // wave-uniform winner
-    if ((c.id & 63) == lane) taken |= 1u << (c.id >> 6);
-    if (j == 0) top0 = c.v;
-    denom += __expf(c.v - top0);
-    if ((j & 63) == lane) { sel[j >> 6] = c.v; sid[j >> 6] = c.id; }
-  }
-#pragma unroll
-  for (int s = 0; s < kSlots; ++s) {
-    const int j = lane + s * kWave;
-    if (j < k) {
-      ids[(int64_t)t * k + j] = sid[s];
-      gates[(int64_t)t * k + j] = __expf(sel[s] - top0) / denom;
-      if (s_hist) atomicAdd(&s_hist[sid[s]], 1);
-      if (s_ids) s_ids[t * k + j] = sid[s];
-    }
-  }
-}
-
-// Tokens t0 + i * step < t1 (i < NT) by one wave: every token's logits
-// are requested first, so the wave waits for memory once, not per token
-// and not per round.
-template <int NT>
-__device__ __forceinline__ void topk_tokens(const float *__restrict__ logits, int t0, int t1, int step, int E, int k,
-                                            int32_t *__restrict__ ids, float *__restrict__ gates, int *s_hist,
-                                            int *s_ids = nullptr) {
-  float v[NT][kSlots];
-#pragma unroll
-  for (int i = 0; i < NT; ++i)
-    if (t0 + i * step < t1) load_logits(logits, t0 + i * step, E, v[i]);
-  // all loads done here: the compiler then knows that no later wait is
-  // needed (it would otherwise wait on each token's stores)
-  vm_wait<0>();
-#pragma unroll
-  for (int i = 0; i < NT; ++i)
-    if (t0 + i * step < t1) topk_token(v[i], t0 + i * step, E, k, ids, gates, s_hist, s_ids);
-}
 
 __global__ void __launch_bounds__(kRouteThreads)
-route_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
-             float *__restrict__ gates, int32_t *__restrict__ offsets,
-             int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ pair_pos) {
-  __shared__ int s_count[kMaxE];
-  __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_run[kMaxE];
-  __shared__ int s_wave[kRouteWaves][kMaxE];
-  __shared__ int s_ids[kRouteTokens * kMaxE];   // the pairs' expert ids
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < kMaxE; e += kRouteThreads) { s_count[e] = 0; s_run[e] = 0; }
-  __syncthreads();
-
-  // ---- phase 1: top-k + gates, one wave per token; the histogram and the
-  // ids also go to LDS, so the later phases read nothing back from memory
-  topk_tokens<kRouteTokens / kRouteWaves>(logits, wave, T, kRouteWaves, E, k, ids, gates, s_count, s_ids);
-  __syncthreads();
-
-  // ---- phase 2: exclusive scan of the histogram
-  const int P = T * k;
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < E; base += kWave) {
-      const int e = base + lane;
-      const int c = e < E ? s_count[e] : 0;
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-      }
-      if (e < E) s_off[e] = carry + incl - c;
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (lane == 0) s_off[E] = carry;
-  }
-  __syncthreads();
-  for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = s_off[e];
-
-  // ---- phase 3: stable placement
-  for (int base = 0; base < P; base += kRouteThreads) {
-    const int p = base + tid;
-    const bool valid = p < P;
-    const int e = valid ? s_ids[p] : 0;
-    // lanes of this wave holding the same expert
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint64_t bal = __ballot(valid && ((e >> b) & 1));
-      peers &= ((e >> b) & 1) ? bal : ~bal;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(peers & below);
-    const bool leader = valid && (peers & below) == 0;
-    for (int x = tid; x < kRouteWaves * kMaxE; x += kRouteThreads) (&s_wave[0][0])[x] = 0;
-    __syncthreads();
-    if (leader) s_wave[wave][e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int before = s_run[e];
-      for (int w = 0; w < wave; ++w) before += s_wave[w][e];
-      const int pos = s_off[e] + before + rank;
-      sorted_pairs[pos] = p;
-      pair_pos[p] = pos;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += kRouteThreads) {
-      int add = 0;
-      for (int w = 0; w < kRouteWaves; ++w) add += s_wave[w][x];
-      s_run[x] += add;
-    }
-    __syncthreads();
-  }
+route_kernel(RouteOut o, int T, int E, int k) {
+  __shared__ RouteLds<kRouteThreads / kWave> s;
+  route_block<kRouteThreads>(o, T, E, k, s);
 }
 
 
@@ -222,7 +34,6 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kSegThreads = 256;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kSegTokens = 64;
-static_assert(kRouteTokens % kRouteWaves == 0, "each wave takes the same number of tokens");
 
 __global__ void __launch_bounds__(kTopkThreads)
 route_topk_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
@@ -396,9 +207,8 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
   prof_begin("route", stream);
   const int nseg = route_segments(T);
   if (route_single(T)) {
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, logits, T, E, k,
-                       out->topk_ids, out->topk_gates, out->expert_offsets, out->sorted_pairs,
-                       out->pair_pos);
+    const RouteOut o{logits, out->topk_ids, out->topk_gates, out->expert_offsets, out->sorted_pairs, out->pair_pos};
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, o, T, E, k);
   } else {
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkThreads), 0, stream,
                        logits, T, E, k, out->topk_ids, out->topk_gates);

@@ -335,8 +335,8 @@ __device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, 
 
 // z of the chunk's pairs in LDS: sums the ks fp32 partials of the
 // projection kernel (all loads issued before any add) and rounds to fp16;
-// with xk the sum is first scaled by 2^K of the row's token (z of the
-// normalised x~ = x 2^K; xexp holds K per sorted position).
+// with xk (gate/up) the sum is first scaled by 2^K of the row's token (z of
+// the normalised x~ = x 2^K).
 // zs layout: [NSUB*16 rows][width] fp16 with width = nset * RZ (RZ padded
 // columns per block); src column base = col0 within each partial row.
 template <int NSUB, int NW>
@@ -347,8 +347,14 @@ __device__ __forceinline__ void z_prologue(const FfnArgs &a, bool xk, const floa
   for (int o = tid; o < n4; o += NW * 64) {
     const int row = (4 * o) / width, col = (4 * o) % width;
     const int m = std::min(row, ch.cnt - 1);
-    const int K = xk ? a.xexp[ch.base + m] : 0;
-    const float *src = zpart + (int64_t)(ch.base + m) * zstride + col;
+    // z rows by sorted position, or (z_tok, gate/up) by token and expert,
+    // zero for a pair outside the token's leading n_comp slots
+    const int pr = a.sorted_pairs[ch.base + m];
+    const int t = pr / a.k;
+    const bool by_tok = xk && a.z_tok;
+    const bool live = !by_tok || pr % a.k < a.n_comp;
+    const int K = xk ? a.xexp[t] : 0;
+    const float *src = zpart + (by_tok ? ((int64_t)t * a.E + ch.e) : (int64_t)(ch.base + m)) * zstride + col;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     int k = 0;
     for (; k + 4 <= KS; k += 4) {
@@ -363,7 +369,7 @@ __device__ __forceinline__ void z_prologue(const FfnArgs &a, bool xk, const floa
       for (int i = 0; i < 4; ++i) sum[i] += v[i];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sum[i] = __builtin_ldexpf(sum[i], K);
+    for (int i = 0; i < 4; ++i) sum[i] = live ? __builtin_ldexpf(sum[i], K) : 0.f;
     u32x2 h;
     h[0] = as_u32(f16x2{(f16)sum[0], (f16)sum[1]});
     h[1] = as_u32(f16x2{(f16)sum[2], (f16)sum[3]});
@@ -626,7 +632,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   preload_two<GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, p0, p1);
   // the rows' x exponents: requested now, kept in one register and put in
   // LDS after the K walk (the epilogue reads them there)
-  const int kreg = threadIdx.x < NSUB * 16 ? a.xexp[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
+  const int kreg = threadIdx.x < NSUB * 16 ? row_kx(a, ch, threadIdx.x) : 0;
   if (a.comp_on) {
     z_prologue<NSUB, 4>(a, true, a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();

@@ -263,7 +263,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   }
   // the rows' x exponents: requested now, stored past the LDS stages after
   // the K walk (so that nothing waits for them)
-  const int kreg = threadIdx.x < kTM ? a.xexp[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
+  const int kreg = threadIdx.x < kTM ? row_kx(a, ch, threadIdx.x) : 0;
   f32x4 acc[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q)

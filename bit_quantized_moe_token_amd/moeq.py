@@ -305,11 +305,13 @@ def plan_reductions(q, bytes_tbl, g, mu, eta, eps, target):
 # ------------------------------------------------------------ expert FFN
 
 class FfnWorkspace:
-    def __init__(self, layer, T, k, path=0, split_k=0):
+    """Workspace of moeq_expert_ffn, or (forward=True) of moeq_moe_forward."""
+
+    def __init__(self, layer, T, k, path=0, split_k=0, forward=False):
         self.opts = _lib.FfnOptions(path, split_k)
         n = ctypes.c_size_t(0)
-        check(lib().moeq_ffn_workspace_size(layer.handle, T, k, ctypes.byref(self.opts), ctypes.byref(n)),
-              "moeq_ffn_workspace_size")
+        size_fn = lib().moeq_forward_workspace_size if forward else lib().moeq_ffn_workspace_size
+        check(size_fn(layer.handle, T, k, ctypes.byref(self.opts), ctypes.byref(n)), "workspace_size")
         self.nbytes = n.value
         self.buf = torch.empty(max(256, n.value), dtype=torch.uint8, device=layer.buf.device)
 
@@ -330,6 +332,27 @@ def expert_ffn(layer, x, routing, n_comp, out=None, out_dtype=torch.float16, ws=
                                 _ptr(out), ydt, _ptr(ws.buf), ws.buf.numel(), ctypes.byref(ws.opts),
                                 _stream()), "moeq_expert_ffn")
     return out
+
+
+def moe_forward(layer, logits, x, k, n_comp, routing=None, out=None, out_dtype=torch.float16, ws=None,
+                path=0, split_k=0):
+    """Routing and the expert FFN in one call (see moeq_moe_forward).
+    Returns (y [T, H], routing)."""
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.float16, (T, layer.H), "x")
+    if routing is None:
+        routing = RoutingOut(T, E, k, x.device)
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=out_dtype, device=x.device)
+    ydt = _lib.F32 if out.dtype == torch.float32 else _lib.F16
+    _need(out, out.dtype, (T, layer.H), "out")
+    if ws is None:
+        ws = FfnWorkspace(layer, T, k, path, split_k, forward=True)
+    check(lib().moeq_moe_forward(layer.handle, _ptr(logits), _ptr(x), T, k, n_comp, ctypes.byref(routing.c),
+                                 _ptr(out), ydt, _ptr(ws.buf), ws.buf.numel(), ctypes.byref(ws.opts), _stream()),
+          "moeq_moe_forward")
+    return out, routing
 
 
 # ------------------------------------------------------------ profiling

@@ -404,6 +404,25 @@ moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int32_t T,
                             const moeq_ffn_options *opts, hipStream_t stream);
 
 /*
+ * moeq_moe_forward — routing and the expert layer in one call: the results
+ * of moeq_route into *r followed by moeq_expert_ffn into y, bit for bit
+ * (same arguments; logits DEVICE [T, E] fp32).  For decode-sized batches
+ * (1 <= T <= 16) of layers with E <= 4 k on the weight-streaming path, the
+ * routing, the activation exponents and the gate/up low-rank projection of
+ * every (token, expert) pair (which needs no routing) share one launch, one
+ * workgroup routing while the others project; other batches run the two calls
+ * in order.  ws DEVICE, at least moeq_forward_workspace_size bytes.
+ * ([MxMoE] abstract: expert activation; [BEAM] abstract: top-n
+ * compensation; the layer of moeq_expert_ffn.)
+ */
+moeq_status moeq_forward_workspace_size(const moeq_layer *L, int32_t T, int32_t k,
+                                        const moeq_ffn_options *opts, size_t *bytes);
+moeq_status moeq_moe_forward(const moeq_layer *L, const float *logits, const uint16_t *x,
+                             int32_t T, int32_t k, int32_t n_comp, const moeq_routing *r,
+                             void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
+                             const moeq_ffn_options *opts, hipStream_t stream);
+
+/*
  * moeq_expert_ffn_noalloc — moeq_expert_ffn for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same
