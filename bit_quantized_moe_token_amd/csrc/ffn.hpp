@@ -36,7 +36,7 @@ struct FfnArgs {
   int8_t *hblk;     // [P][hblk_stride] eb (h_block_exp), I/64 used per row
   int hblk_stride;  // bytes per row of hblk (I/64 rounded up to 16)
   uint16_t *hn;     // [P][I] fp16: h * 2^(kNormTop - eh), eh = the pair's largest eb
-  int32_t *hexp;    // [P] eh
+  int32_t *hexp;    // [P] eh (set to kHZero by the first launch, raised by the gate/up kernels)
   int32_t *xexp;    // [T] K of each token (x_norm_exp)
   uint16_t *xn;     // [T][H] x * 2^K, the activations the gate/up kernels read
   float *ypart;     // [splits][P][H] fp32, in units of 2^(eh - kNormTop) (the combine undoes it)
@@ -103,9 +103,12 @@ __device__ __forceinline__ int h_block_exp(float mx) {
 
 // x exponents of tokens t = wid, wid + nw, ...: one wave per token takes
 // the largest |x| of the row (fp16 magnitude bits compare as integers),
-// writes K = x_norm_exp of its exponent and the row x 2^K to xn.
+// writes K = x_norm_exp of its exponent and the row x 2^K to xn.  The same
+// waves set every pair's h exponent eh to kHZero, the start of the maximum
+// that the gate/up kernels take over their blocks (h_pair_exp).
 __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   const int lane = threadIdx.x & 63;
+  for (int i = wid * kWave + lane; i < a.P; i += nw * kWave) a.hexp[i] = kHZero;
   for (int t = wid; t < a.T; t += nw) {
     const uint16_t *row = a.x + (int64_t)t * a.H;
     uint32_t m = 0;
@@ -125,29 +128,10 @@ __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   }
 }
 
-// eh of 16 pairs (sorted positions pos0 .. pos0 + 15, clamped to
-// pos_last), computed by the workgroup's 256 threads: thread tid takes row
-// tid / 16 and, per 256 blocks, 16 consecutive block exponents (one 16-byte
-// load; blocks past I/64 ignored), then a DPP row maximum into s_eh[16].
-// With s_eb (used when I/64 <= 256) the exponents are also kept in LDS,
-// s_eb[row * 256 + block].  The caller synchronises before reading them.
-__device__ __forceinline__ void pair_eh16(const FfnArgs &a, int pos0, int pos_last, int *s_eh, int8_t *s_eb) {
-  const int tid = threadIdx.x;
-  const int r = tid >> 4, nb = a.I / 64;
-  const int pos = std::min(pos0 + r, pos_last);
-  int e = kHZero;
-  for (int j0 = 16 * (tid & 15); j0 < nb; j0 += 256) {
-    const u32x4 v = gld<u32x4>(a.hblk + (int64_t)pos * a.hblk_stride + j0);
-    if (s_eb) *reinterpret_cast<u32x4 *>(s_eb + r * 256 + j0) = v;
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const int eb = (int)(int8_t)(v[b >> 2] >> (8 * (b & 3)));
-      if (j0 + b < nb) e = std::max(e, eb);
-    }
-  }
-  e = dpp_row_max(e);
-  if ((tid & 15) == 0) s_eh[r] = e;
-}
+// eh of the pair at sorted position pos = the largest eb over its blocks:
+// each gate/up workgroup raises it to the eb of the block it wrote (an
+// integer maximum, so the result does not depend on the order).
+__device__ __forceinline__ void h_pair_exp(const FfnArgs &a, int pos, int eb) { atomicMax(a.hexp + pos, eb); }
 
 // x exponent of chunk row m (rows past the count repeat the last one).
 __device__ __forceinline__ int row_kx(const FfnArgs &a, const Chunk &ch, int m) {

@@ -23,17 +23,15 @@ namespace moeq {
 // pair (grid.x = ceil(T / 16) * E), which needs no routing; in both the
 // extra y slice (blockIdx.y == njy) computes the tokens' x exponents
 // instead.  mode 1: v = h of the pair, renormalised on the fly from its
-// per-block exponents to the pair's exponent eh; the workgroups of y slice
-// 0 also store that renormalised h (hn) and eh, which the down kernels and
-// the combine read.
+// per-block exponents to the pair's exponent eh (final once the gate/up
+// kernel has run); the workgroups of y slice 0 also store that
+// renormalised h (hn), which the down kernels read.
 // ROUTE (mode 2 only): one more y slice, whose first workgroup routes the
 // tokens (route_block) while the others project; the projection of every
 // (token, expert) pair needs no routing, so both fit in one launch.
 template <int NJ, bool ROUTE>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy, RouteOut ro) {
   __shared__ f32x4 s_part[4][NJ][64];
-  __shared__ int s_eh[16];
-  __shared__ __attribute__((aligned(16))) int8_t s_eb[16 * 256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (mode != 1 && (int)blockIdx.y >= njy) {
     if constexpr (ROUTE) {
@@ -61,15 +59,8 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     if (!find_chunk(a.offsets, a.E, blockIdx.x / kSubPerChunk, &ch)) return;
   }
   if (16 * sub >= ch.cnt) return;
-  // mode 1: eh of the tile's 16 pairs; y slice 0 writes hn and eh
+  // mode 1: y slice 0 writes hn
   const bool write_hn = mode == 1 && blockIdx.y == 0;
-  const bool eb_lds = a.I / 64 <= 256;
-  if (mode == 1) {
-    pair_eh16(a, ch.base + 16 * sub, ch.base + ch.cnt - 1, s_eh, eb_lds ? s_eb : nullptr);
-    __syncthreads();
-    if (write_hn && blockIdx.z == 0 && threadIdx.x < 16 && 16 * sub + (int)threadIdx.x < ch.cnt)
-      a.hexp[ch.base + 16 * sub + threadIdx.x] = s_eh[threadIdx.x];
-  }
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
   const bool gu = mode != 1;
   const int K = gu ? a.H : a.I;
@@ -122,13 +113,14 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   // mode 1: the lane's row of h is renormalised per 64-column block by
   // 2^(eb - eh) (32-column steps st lie in block st / 2); y slice 0 stores
   // the result for the rows of the chunk
-  const int eh = mode == 1 ? s_eh[lane & 15] : 0;
-  const int8_t *ebrow = eb_lds ? s_eb + (lane & 15) * 256 : a.hblk + (int64_t)pos * a.hblk_stride;
+  const int eh = mode == 1 ? a.hexp[pos] : 0;
+  const int8_t *ebrow = a.hblk + (int64_t)pos * a.hblk_stride;
   uint16_t *hnrow = a.hn + (int64_t)pos * a.I + 8 * (lane >> 4);
   const bool store_hn = write_hn && 16 * sub + (lane & 15) < ch.cnt;
-  // mode 1: h fragment of step st renormalised to eh (and stored by slice 0)
-  auto renorm = [&](f16x8 v, int st) -> f16x8 {
-    const u32x4 w = scale_f16x8(__builtin_bit_cast(u32x4, v), f16x2_pow2((int)ebrow[st >> 1] - eh));
+  // mode 1: h fragment of step st (block exponent eb) renormalised to eh
+  // (and stored by slice 0)
+  auto renorm = [&](f16x8 v, int st, int eb) -> f16x8 {
+    const u32x4 w = scale_f16x8(__builtin_bit_cast(u32x4, v), f16x2_pow2(eb - eh));
     if (store_hn) *reinterpret_cast<u32x4 *>(hnrow + 32 * st) = w;
     return __builtin_bit_cast(f16x8, w);
   };
@@ -145,15 +137,19 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   int st = s0;
   for (; st + BATCH <= s1; st += BATCH) {
     f16x8 av[BATCH], bv[BATCH][NJ];
+    int eb[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       av[u] = load_a(arow + 32 * (st + u));
+      // (the block exponents are loaded with the fragments: a byte load
+      // after the first hn store would have to wait for it)
+      if (mode == 1) eb[u] = ebrow[(st + u) >> 1];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bv[u][j] = vi[j] ? load_a(vrow[j] + 32 * (st + u)) : zero;
     }
     if (mode == 1)
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) av[u] = renorm(av[u], st + u);
+      for (int u = 0; u < BATCH; ++u) av[u] = renorm(av[u], st + u, eb[u]);
 #pragma unroll
     for (int u = 0; u < BATCH; u += 2)
 #pragma unroll
@@ -164,7 +160,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   }
   for (; st < s1; ++st) {
     f16x8 av = load_a(arow + 32 * st);
-    if (mode == 1) av = renorm(av, st);
+    if (mode == 1) av = renorm(av, st, ebrow[st >> 1]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = mfma16(av, vi[j] ? load_a(vrow[j] + 32 * st) : zero, acc[j]);
   }
@@ -298,14 +294,10 @@ __global__ void __launch_bounds__(256) xexp_kernel(FfnArgs a) {
   xexp_rows(a, (int)blockIdx.x * 4 + (threadIdx.x >> 6), (int)gridDim.x * 4);
 }
 
-// hn and eh when no down projection runs: 16 pairs (sorted positions) per
+// hn when no down projection runs: 16 pairs (sorted positions) per
 // workgroup; each thread rescales 16-byte pieces of the rows.
 __global__ void __launch_bounds__(256) hnorm_kernel(FfnArgs a) {
-  __shared__ int s_eh[16];
   const int pos0 = (int)blockIdx.x * 16;
-  pair_eh16(a, pos0, a.P - 1, s_eh, nullptr);
-  __syncthreads();
-  if (threadIdx.x < 16 && pos0 + (int)threadIdx.x < a.P) a.hexp[pos0 + threadIdx.x] = s_eh[threadIdx.x];
   const int per_row = a.I / 8;
   for (int i = threadIdx.x; i < 16 * per_row; i += 256) {
     const int r = i / per_row, c = (i % per_row) * 8;
@@ -313,7 +305,7 @@ __global__ void __launch_bounds__(256) hnorm_kernel(FfnArgs a) {
     if (pos >= a.P) break;
     const int64_t off = (int64_t)pos * a.I + c;
     const int eb = gld<int8_t>(a.hblk + (int64_t)pos * a.hblk_stride + c / 64);
-    *reinterpret_cast<u32x4 *>(a.hn + off) = scale_f16x8(gld<u32x4>(a.h + off), f16x2_pow2(eb - s_eh[r]));
+    *reinterpret_cast<u32x4 *>(a.hn + off) = scale_f16x8(gld<u32x4>(a.h + off), f16x2_pow2(eb - a.hexp[pos]));
   }
 }
 

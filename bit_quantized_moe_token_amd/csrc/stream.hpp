@@ -702,7 +702,10 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
         o[2 + j] = as_u32(f16x2{(f16)__builtin_ldexpf(v1[2 * j], kNormTop - eb), (f16)__builtin_ldexpf(v1[2 * j + 1], kNormTop - eb)});
       }
       *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + m) * a.I + 64 * sg + c8) = o;
-      if ((tid & 7) == 0) a.hblk[(int64_t)(ch.base + m) * a.hblk_stride + sg] = (int8_t)eb;
+      if ((tid & 7) == 0) {
+        a.hblk[(int64_t)(ch.base + m) * a.hblk_stride + sg] = (int8_t)eb;
+        h_pair_exp(a, ch.base + m, eb);
+      }
     }
   }
 }

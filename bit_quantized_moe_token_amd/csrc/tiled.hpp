@@ -351,6 +351,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
       }
       *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + r) * a.I + nt * kTileK + c8) = o;
       if ((tid & 15) < 2) a.hblk[(int64_t)(ch.base + r) * a.hblk_stride + 2 * nt + (tid & 15)] = (int8_t)eb;
+      if ((tid & 15) == 0) h_pair_exp(a, ch.base + r, eb);
     }
   }
 }
