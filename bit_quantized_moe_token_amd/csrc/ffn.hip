@@ -157,10 +157,7 @@ static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, 
 static void ffn_front(const FfnArgs &a, hipStream_t stream) {
   if (a.comp_on) {
     prof_begin("lowrank_project_gu", stream);
-    if (a.z_tok)
-      launch_lowrank_project(a, 2, dim3((a.T + 15) / 16 * a.E, 2 * a.RZ / 16), stream);
-    else
-      launch_lowrank_project(a, 0, dim3(max_chunks(a.E, a.T, a.k) * kSubPerChunk, 2 * a.RZ / 16), stream);
+    launch_lowrank_project(a, a.z_tok ? 2 : 0, 2 * a.RZ / 16, stream);
     prof_end("lowrank_project_gu", stream);
   } else {
     prof_begin("xexp", stream);
@@ -187,7 +184,7 @@ static moeq_status ffn_rest(const FfnArgs &a, int path, void *y, int32_t y_dtype
   // there is one)
   if (a.comp_on) {
     prof_begin("lowrank_project_down", stream);
-    launch_lowrank_project(a, 1, dim3(mc * kSubPerChunk, a.RZ / 16), stream);
+    launch_lowrank_project(a, 1, a.RZ / 16, stream);
     prof_end("lowrank_project_down", stream);
   } else {
     prof_begin("hnorm", stream);

@@ -153,7 +153,7 @@ struct RouteOut;   // route.hpp
 // Launchers (stream.hip, lowrank.hip).
 void launch_gateup_stream(const FfnArgs &a, int grid, hipStream_t s);
 void launch_down_stream(const FfnArgs &a, int grid, hipStream_t s);
-void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s);
+void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s);   // jobs: 16-column jobs
 void launch_front_routed(const FfnArgs &a, const RouteOut &ro, hipStream_t s);   // needs a.z_tok, a.T <= kRouteTokens
 void launch_combine(const FfnArgs &a, void *y, bool f32, hipStream_t s);
 void launch_xexp(const FfnArgs &a, hipStream_t s);    // x exponents alone (no gate/up projection)

@@ -29,6 +29,8 @@ namespace moeq {
 // ROUTE (mode 2 only): one more y slice, whose first workgroup routes the
 // tokens (route_block) while the others project; the projection of every
 // (token, expert) pair needs no routing, so both fit in one launch.
+// A tile none of whose pairs is compensated (router-guided top-n) loads
+// no V and writes zero rows.
 template <int NJ, bool ROUTE>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy, RouteOut ro) {
   __shared__ f32x4 s_part[4][NJ][64];
@@ -59,6 +61,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     if (!find_chunk(a.offsets, a.E, blockIdx.x / kSubPerChunk, &ch)) return;
   }
   if (16 * sub >= ch.cnt) return;
+  // the tile's pairs (rows past the count repeat the last one)
+  const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
+  const int pos = ch.base + mloc;
+  // by sorted position: a pair outside its token's leading n_comp slots
+  // gets a zero row; by token (mode 2) the consumer applies that mask
+  const bool comp_row = tok || (a.sorted_pairs[pos] % a.k) < a.n_comp;
+  const bool tile_comp = __ballot(comp_row) != 0;   // the same in every wave of the tile
   // mode 1: y slice 0 writes hn
   const bool write_hn = mode == 1 && blockIdx.y == 0;
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
@@ -91,9 +100,8 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     vi[j] = live[j] && i < R;
     vrow[j] = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
   }
-  // (y slice 0 always holds a live job: rank tile 0 of the first factor set
-  // with a nonzero rank, so the workgroups that store hn never exit here)
-  if (!any) {
+  // zero z rows for the tile (by wave 0)
+  auto zero_rows = [&]() {
     if (wave == 0)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -102,10 +110,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
 #pragma unroll
           for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = 0.0f;
       }
+  };
+  // (y slice 0 always holds a live job: rank tile 0 of the first factor set
+  // with a nonzero rank, so the workgroups that store hn never exit here)
+  if (!any) {
+    zero_rows();
     return;
   }
-  const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
-  const int pos = ch.base + mloc;
   const uint16_t *arow = mode == 0 ? a.x + (int64_t)(a.sorted_pairs[pos] / a.k) * a.H
                          : mode == 2 ? a.x + (int64_t)pos * a.H
                                      : a.h + (int64_t)pos * a.I;
@@ -127,6 +138,27 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const int nsteps = K / 32;
   const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
   const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
+  // no pair of the tile compensated (router-guided top-n): zero z rows, no
+  // V loads; in mode 1 slice 0 still stores the tile's renormalised h
+  if (!tile_comp) {
+    zero_rows();
+    if (write_hn) {
+      int st = s0;
+      for (; st + 8 <= s1; st += 8) {
+        f16x8 v[8];
+        int e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          v[u] = load_a(arow + 32 * (st + u));
+          e[u] = ebrow[(st + u) >> 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) (void)renorm(v[u], st + u, e[u]);
+      }
+      for (; st < s1; ++st) (void)renorm(load_a(arow + 32 * st), st, ebrow[st >> 1]);
+    }
+    return;
+  }
   // batches of BATCH steps: all their fragment loads are issued before the
   // first MFMA, so each batch waits for memory once
   constexpr int BATCH = NJ >= 8 ? 2 : 8 / NJ;
@@ -168,8 +200,9 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] += acc2[j][q];
-    s_part[wave][j][lane] = acc[j];
   }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) s_part[wave][j][lane] = acc[j];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
@@ -187,8 +220,6 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   for (int q = 0; q < 4; ++q) {
     const int m = 16 * sub + 4 * (lane >> 4) + q;
     if (m < ch.cnt) {
-      // by sorted position: zero for a pair outside its token's leading
-      // n_comp slots; by token (mode 2) the consumer applies that mask
       const bool comp = tok || (a.sorted_pairs[ch.base + m] % a.k) < a.n_comp;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
@@ -259,8 +290,9 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
   }
 }
 
-void launch_lowrank_project(const FfnArgs &a, int mode, dim3 grid, hipStream_t s) {
-  grid.z = mode != 1 ? a.ks_gu : a.ks_d;
+void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s) {
+  dim3 grid(mode == 2 ? (a.T + 15) / 16 * a.E : max_chunks(a.E, a.T, a.k) * kSubPerChunk, jobs,
+            mode != 1 ? a.ks_gu : a.ks_d);
   // two, four or eight jobs per workgroup when many tokens leave no K
   // split (the activation re-reads dominate; fewer jobs keep enough
   // workgroups); the job count is always even

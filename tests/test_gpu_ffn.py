@@ -82,6 +82,29 @@ def test_ffn_compensation_switch(case):
         layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, n_comp), f"{case} n_comp={n_comp}")
 
 
+@pytest.mark.parametrize("case,path", [("decode", PATH_STREAM), ("prefill", PATH_STREAM),
+                                       ("prefill", PATH_TILED), ("finegrained", PATH_AUTO)])
+def test_ffn_expert_reached_only_by_uncompensated_slots(case, path):
+    """Router-guided top-n compensation with n_comp = 1 when one expert is
+    every token's second choice: all of its pairs are uncompensated, so its
+    tiles skip the low-rank projections (zero z rows, no V loads; the down
+    projection still stores their renormalised h).  Parity with the oracle,
+    on few pairs (one 16-pair tile per workgroup) and on many (a 64-pair
+    chunk per workgroup), streaming and tiled."""
+    from bit_quantized_moe_token_amd import moeq
+    cfg, orc, dev, x, logits = _setup(case)
+    assert cfg["k"] >= 2
+    lg = logits.copy()
+    e2 = cfg["E"] - 1
+    others = np.sort(np.delete(lg, e2, axis=1), axis=1)
+    lg[:, e2] = ((others[:, -1].astype(np.float64) + others[:, -2]) / 2).astype(np.float32)
+    rt = moeq.route(torch.from_numpy(lg).cuda(), cfg["k"])
+    ids = rt.ids.cpu().numpy()
+    assert (ids[:, 1] == e2).all() and (ids[:, 0] != e2).all()
+    y = _run(dev, cfg, x, lg, 1, out_dtype=torch.float32, path=path)
+    layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, cfg, x, lg, 1), f"{case} second-choice expert n_comp=1")
+
+
 def test_rank0_bitwise_equals_uncompensated():
     from bit_quantized_moe_token_amd import moeq
     cfg, orc, dev, x, logits = _setup("tiny")
