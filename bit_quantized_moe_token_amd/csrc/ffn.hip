@@ -3,7 +3,7 @@
 //
 //   project V x (gate/up) + x exponents -> gate/up + SwiGLU (h with block
 //   exponents) -> project V_down h + h renormalised per pair -> down
-//   (split-K partials) -> gate-weighted combine (undoes the h exponent)
+//   (gate-scaled split-K partials) -> combine (undoes the h exponent)
 #include "common.hpp"
 #include "ffn.hpp"
 #include "route.hpp"
@@ -14,7 +14,7 @@ namespace moeq {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
-  size_t zp_gu, zp_d, h, hblk, hn, hexp, xexp, xn, ypart, total;
+  size_t zp_gu, zp_d, zsh, dlead, h, hblk, hn, hexp, hexpf, xexp, xn, ypart, total;
   int ks_gu, ks_d;
 };
 
@@ -82,10 +82,13 @@ static Ws ws_plan(const moeq_layer *L, int T, int k, int splits, bool z_tok = fa
   size_t off = 0;
   w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * PZ * 2 * RZ * 4);
   w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
+  w.zsh = off; off = al256(off + (size_t)w.ks_d * P * k * Rsp * 4);
+  w.dlead = off; off = al256(off + (Rsp ? (size_t)P * 4 : 0));
   w.h = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.hblk = off; off = al256(off + (size_t)P * hblk_stride(L));
   w.hn = off; off = al256(off + (size_t)P * L->dims.I * 2);
   w.hexp = off; off = al256(off + (size_t)P * 4);
+  w.hexpf = off; off = al256(off + (size_t)P * 4);
   w.xexp = off; off = al256(off + (size_t)T * 4);
   w.xn = off; off = al256(off + (size_t)T * L->dims.H * 2);
   w.ypart = off; off = al256(off + (size_t)splits * P * L->dims.H * 4);
@@ -111,6 +114,10 @@ static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, 
   if (T == 0) return MOEQ_OK;
   if (!x || !y || !r->topk_gates || !r->expert_offsets || !r->sorted_pairs || !r->pair_pos)
     return fail(MOEQ_ERR_INVALID, "expert_ffn: null pointer");
+  if (D.rs > 0 && n_comp > 0 && !r->topk_ids)
+    return fail(MOEQ_ERR_INVALID, "expert_ffn: a layer with shared factors needs the routing's topk_ids");
+  if (D.rs > 0 && n_comp > 32)
+    return fail(MOEQ_ERR_UNSUPPORTED, "expert_ffn: shared factors with n_comp=%d > 32 compensated slots", n_comp);
   const int splits = pick_splits(L, T, k, opts);
   const Ws w = ws_plan(L, T, k, splits, z_tok);
   if (!ws || ws_bytes < w.total)
@@ -124,12 +131,17 @@ static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, 
   a.x = x;
   a.gates = r->topk_gates;
   a.pair_pos = r->pair_pos;
+  a.ids = r->topk_ids;
+  a.share = D.rs > 0 ? D.share : 1;
   a.E = D.E; a.H = D.H; a.I = D.I; a.k = k; a.T = T; a.n_comp = n_comp;
   a.r = D.r; a.rs = D.rs;
   a.Rp = (D.r + 31) / 32 * 32; a.Rsp = (D.rs + 31) / 32 * 32; a.RZ = a.Rp + a.Rsp;
   a.comp_on = (n_comp > 0 && a.RZ > 0) ? 1 : 0;
   a.zp_gu = reinterpret_cast<float *>(wb + w.zp_gu);
   a.zp_d = reinterpret_cast<float *>(wb + w.zp_d);
+  a.zsh = reinterpret_cast<float *>(wb + w.zsh);
+  a.dlead = reinterpret_cast<int32_t *>(wb + w.dlead);
+  a.ks_stride_sh = (int64_t)T * k * k * ((D.rs + 31) / 32 * 32);
   a.z_tok = z_tok ? 1 : 0;
   a.ks_gu = w.ks_gu;
   a.ks_d = w.ks_d;
@@ -140,6 +152,7 @@ static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, 
   a.hblk_stride = hblk_stride(L);
   a.hn = reinterpret_cast<uint16_t *>(wb + w.hn);
   a.hexp = reinterpret_cast<int32_t *>(wb + w.hexp);
+  a.hexpf = reinterpret_cast<int32_t *>(wb + w.hexpf);
   a.xexp = reinterpret_cast<int32_t *>(wb + w.xexp);
   a.xn = reinterpret_cast<uint16_t *>(wb + w.xn);
   a.ypart = reinterpret_cast<float *>(wb + w.ypart);

@@ -22,6 +22,8 @@ struct FfnArgs {
   const uint16_t *x;
   const float *gates;
   const int32_t *pair_pos;
+  const int32_t *ids;   // [T][k] expert of each slot (read with shared factors only)
+  int share;            // experts per shared-factor group (1 without shared factors)
   int E, H, I, k, T, n_comp;
   int r, rs, Rp, Rsp, RZ;
   int comp_on;
@@ -29,14 +31,20 @@ struct FfnArgs {
   float *zp_gu;     // [ks_gu][P][2][RZ] fp32 partial V x (summed by the consumer), by sorted
                     // position; with z_tok [ks_gu][T][E][2][RZ] by (token, expert), every pair
   int z_tok;
-  float *zp_d;      // [ks_d][P][RZ] fp32 partial V_down h
+  float *zp_d;      // [ks_d][P][RZ] fp32 partial V_down h (per-expert columns)
+  float *zsh;       // [ks_d][P][k][Rsp] fp32: shared columns, row of the down leader of
+                    // (token, group), sub-row = the member's slot (see slot_group)
+  int32_t *dlead;   // [P] member mask of a down leader, 0 for the other pairs
+  int64_t ks_stride_sh;
   int ks_gu, ks_d;  // K splits of the two projections
   int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
   uint16_t *h;      // [P][I] fp16: h * 2^(kNormTop - eb), eb per (pair, 64-row block of I)
   int8_t *hblk;     // [P][hblk_stride] eb (h_block_exp), I/64 used per row
   int hblk_stride;  // bytes per row of hblk (I/64 rounded up to 16)
   uint16_t *hn;     // [P][I] fp16: h * 2^(kNormTop - eh), eh = the pair's largest eb
-  int32_t *hexp;    // [P] eh (set to kHZero by the first launch, raised by the gate/up kernels)
+  int32_t *hexp;    // [P] eh by sorted position (set to kHZero by the first launch, raised by
+                    // the gate/up kernels)
+  int32_t *hexpf;   // [P] the same by pair id t*k + j
   int32_t *xexp;    // [T] K of each token (x_norm_exp)
   uint16_t *xn;     // [T][H] x * 2^K, the activations the gate/up kernels read
   float *ypart;     // [splits][P][H] fp32, in units of 2^(eh - kNormTop) (the combine undoes it)
@@ -108,7 +116,7 @@ __device__ __forceinline__ int h_block_exp(float mx) {
 // that the gate/up kernels take over their blocks (h_pair_exp).
 __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   const int lane = threadIdx.x & 63;
-  for (int i = wid * kWave + lane; i < a.P; i += nw * kWave) a.hexp[i] = kHZero;
+  for (int i = wid * kWave + lane; i < a.P; i += nw * kWave) a.hexp[i] = a.hexpf[i] = kHZero;
   for (int t = wid; t < a.T; t += nw) {
     const uint16_t *row = a.x + (int64_t)t * a.H;
     uint32_t m = 0;
@@ -128,14 +136,80 @@ __device__ __forceinline__ void xexp_rows(const FfnArgs &a, int wid, int nw) {
   }
 }
 
-// eh of the pair at sorted position pos = the largest eb over its blocks:
-// each gate/up workgroup raises it to the eb of the block it wrote (an
-// integer maximum, so the result does not depend on the order).
-__device__ __forceinline__ void h_pair_exp(const FfnArgs &a, int pos, int eb) { atomicMax(a.hexp + pos, eb); }
+// eh of the pair p at sorted position pos = the largest eb over its
+// blocks: each gate/up workgroup raises it to the eb of the block it wrote
+// (an integer maximum, so the result does not depend on the order); kept
+// by position and by pair id.
+__device__ __forceinline__ void h_pair_exp(const FfnArgs &a, int pos, int p, int eb) {
+  atomicMax(a.hexp + pos, eb);
+  atomicMax(a.hexpf + p, eb);
+}
 
-// x exponent of chunk row m (rows past the count repeat the last one).
-__device__ __forceinline__ int row_kx(const FfnArgs &a, const Chunk &ch, int m) {
-  return a.xexp[a.sorted_pairs[ch.base + std::min(m, ch.cnt - 1)] / a.k];
+// Shared factors (TileQ abstract: factors shared by a group of experts).
+// The compensated slots of token t whose experts lie in group G, as a slot
+// mask (n_comp <= 32 with shared factors), and the slot that carries the
+// group's work for the token (its leader):
+//   gate/up: the first member; it computes V_G x once for (t, G) and
+//   writes it into the z rows of every member;
+//   down (DOWN): the member m of largest g_m 2^eh_m (its key
+//   eh_m + log2 g_m; ties to the lower slot).  U_G is applied once, in the
+//   leader's row, to w' = sum over members m of f_m V_G hn_m with
+//   f_m = g_m 2^eh_m / (g_lead 2^eh_lead) <= 1 (hn_m = h_m 2^(kNormTop -
+//   eh_m)); the combine's factor g_lead 2^(eh_lead - kNormTop) for the
+//   leader's row then gives sum_m g_m U_G V_G h_m, and w' never exceeds
+//   the size of the z rows.
+struct SlotGroup {
+  uint32_t mask;
+  int lead;       // slot
+  int lead_pos;   // DOWN: sorted position of the leader
+  float key;      // DOWN: the leader's key
+};
+
+__device__ __forceinline__ float down_key(float g, int eh) {
+  return g > 0.f ? (float)eh + __builtin_log2f(g) : -__builtin_inff();
+}
+
+template <bool DOWN>
+__device__ __forceinline__ SlotGroup slot_group(const FfnArgs &a, int t, int G) {
+  SlotGroup g{0u, -1, 0, -__builtin_inff()};
+  const int64_t row = (int64_t)t * a.k;
+  for (int j0 = 0; j0 < a.n_comp; j0 += 8) {
+    // a batch of eight slots: every load issued before the first use (all
+    // indexed by pair id, so none waits for another)
+    int id[8], pp[8], eh[8];
+    float gv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = j0 + u < a.n_comp;
+      id[u] = ok ? a.ids[row + j0 + u] : -1;
+      pp[u] = (DOWN && ok) ? a.pair_pos[row + j0 + u] : 0;
+      gv[u] = (DOWN && ok) ? a.gates[row + j0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) eh[u] = (DOWN && j0 + u < a.n_comp) ? a.hexpf[row + j0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (id[u] < 0 || id[u] / a.share != G) continue;
+      g.mask |= 1u << (j0 + u);
+      if (!DOWN) {
+        if (g.lead < 0) g.lead = j0 + u;
+      } else {
+        const float key = down_key(gv[u], eh[u]);
+        if (g.lead < 0 || key > g.key) {
+          g.key = key;
+          g.lead = j0 + u;
+          g.lead_pos = pp[u];
+        }
+      }
+    }
+  }
+  return g;
+}
+
+// f_m of a member with key `key` in a group whose leader has key `lead`
+// (0 when every member's gate is 0).
+__device__ __forceinline__ float down_factor(float key, float lead) {
+  return lead == -__builtin_inff() ? 0.f : __builtin_exp2f(key - lead);
 }
 
 // Upper bound of the number of chunks of MT pairs for T tokens, top-k, E

@@ -1,10 +1,11 @@
-// Skinny low-rank projections and the gate-weighted combine.
+// Skinny low-rank projections and the combine.
 //
 // z = V v for each compensated pair (MiLo abstract: low-rank compensators;
-// TileQ abstract: factors shared by a group of experts, so each pair also
-// gets the group's V_G v; Bandwidth-Efficient Adaptive MoE abstract: only a
-// token's top-n slots are compensated, the other rows of z are zero), and
-// y_t = sum_j g_{t,j} y_pair(t, j) summed in slot order.
+// TileQ abstract: factors shared by a group of experts, so a pair also
+// gets the group's V_G v, once per (token, group) on the gate/up side;
+// Bandwidth-Efficient Adaptive MoE abstract: only a token's top-n slots are
+// compensated, the other rows of z are zero), and y_t = sum_j g_{t,j}
+// y_pair(t, j) summed in slot order.
 #include "common.hpp"
 #include "ffn.hpp"
 #include "route.hpp"
@@ -68,10 +69,34 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   // gets a zero row; by token (mode 2) the consumer applies that mask
   const bool comp_row = tok || (a.sorted_pairs[pos] % a.k) < a.n_comp;
   const bool tile_comp = __ballot(comp_row) != 0;   // the same in every wave of the tile
+  const bool gu = mode != 1;
+  // shared factors (see slot_group): the group of the lane's row — its
+  // member mask, whether the row leads it and (mode 1) the leader's
+  // position and the row's factor f — requested now and handed to the
+  // store phase through LDS after the main loop.  Gate/up: V_G x is
+  // computed for every row of a tile; only the leader of each (token,
+  // group) stores it, into the rows of all members (mode 2: the group's
+  // first expert, for the group's experts).
+  int gmask = 0, glead = 0, gpos = 0;
+  float gf = 0.f;
+  if (a.rs > 0 && !tok && comp_row) {
+    const int p = a.sorted_pairs[pos];
+    const int t = p / a.k, j = p % a.k;
+    if (gu) {
+      const SlotGroup sg = slot_group<false>(a, t, ch.e / a.share);
+      gmask = (int)sg.mask;
+      glead = sg.lead == j;
+    } else {
+      const SlotGroup sg = slot_group<true>(a, t, ch.e / a.share);
+      gmask = (int)sg.mask;
+      glead = sg.lead == j;
+      gpos = sg.lead_pos;
+      gf = down_factor(down_key(a.gates[p], a.hexpf[p]), sg.key);
+    }
+  }
   // mode 1: y slice 0 writes hn
   const bool write_hn = mode == 1 && blockIdx.y == 0;
   const int jobs_per_blk = (a.Rp + a.Rsp) / 16;
-  const bool gu = mode != 1;
   const int K = gu ? a.H : a.I;
   const int KS = gu ? a.ks_gu : a.ks_d;
   float *zbase = gu ? a.zp_gu + blockIdx.z * a.ks_stride_gu : a.zp_d + blockIdx.z * a.ks_stride_d;
@@ -79,7 +104,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   // output row of chunk row m: its sorted position, or (mode 2) token * E + e
   auto zrow = [&](int m) -> int64_t { return tok ? (int64_t)m * a.E + ch.e : (int64_t)(ch.base + m); };
   int zcol[NJ];
-  bool live[NJ], vi[NJ];
+  bool live[NJ], vi[NJ], shj[NJ];
   const uint16_t *vrow[NJ];
   bool any = false;
 #pragma unroll
@@ -94,13 +119,15 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     zcol[j] = bi * a.RZ + set * a.Rp + 16 * it + (lane & 15);
     // a job wholly in the rank padding (rank 8 or 16 padded to 32) loads
     // nothing and writes zero rows
+    shj[j] = gu && set == 1;
     live[j] = 16 * it < R;
     any = any || live[j];
     const int i = 16 * it + (lane & 15);
     vi[j] = live[j] && i < R;
     vrow[j] = V + (int64_t)std::min(i, R - 1) * K + 8 * (lane >> 4);
   }
-  // zero z rows for the tile (by wave 0)
+  // zero z rows for the tile (by wave 0; shared columns are written by the
+  // groups' leaders, and their readers mask uncompensated pairs)
   auto zero_rows = [&]() {
     if (wave == 0)
 #pragma unroll
@@ -108,11 +135,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
         const int m = 16 * sub + 4 * (lane >> 4) + q;
         if (m < ch.cnt)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = 0.0f;
+          for (int j = 0; j < NJ; ++j)
+            if (!shj[j] && !(mode == 1 && zcol[j] >= a.Rp)) zbase[zrow(m) * zstride + zcol[j]] = 0.0f;
       }
   };
-  // (y slice 0 always holds a live job: rank tile 0 of the first factor set
-  // with a nonzero rank, so the workgroups that store hn never exit here)
+  // (y slice 0 always holds a live job in mode 1: rank tile 0 of the first
+  // factor set with a nonzero rank, so the workgroups that store hn never
+  // exit here)
   if (!any) {
     zero_rows();
     return;
@@ -203,6 +232,13 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s_part[wave][j][lane] = acc[j];
+  __shared__ int s_grp[16][4];
+  if (wave == 0 && lane < 16) {
+    s_grp[lane][0] = gmask;
+    s_grp[lane][1] = glead;
+    s_grp[lane][2] = gpos;
+    s_grp[lane][3] = __builtin_bit_cast(int, gf);
+  }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
@@ -216,13 +252,58 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     }
     acc[j] = sum;
   }
+  // does this workgroup hold shared jobs (mode 1: the first one writes the
+  // leader masks)
+  bool any_sh = false, dl_writer = false;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bool sh1 = mode == 1 && zcol[j] >= a.Rp;
+    any_sh = any_sh || shj[j] || sh1;
+    if (sh1 && zcol[j] - (lane & 15) == a.Rp && blockIdx.z == 0) dl_writer = true;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 16 * sub + 4 * (lane >> 4) + q;
     if (m < ch.cnt) {
-      const bool comp = tok || (a.sorted_pairs[ch.base + m] % a.k) < a.n_comp;
+      // (mode 2 runs beside the routing: it reads no routing array)
+      const int p = tok ? 0 : a.sorted_pairs[ch.base + m];
+      const bool comp = tok || (p % a.k) < a.n_comp;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
+      for (int j = 0; j < NJ; ++j)
+        if (!shj[j] && !(mode == 1 && zcol[j] >= a.Rp))
+          zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
+      if (!any_sh || !comp) continue;
+      const int r = m - 16 * sub;
+      if (gu) {
+        // the leader writes V_G x into the row of every member of its group
+        if (tok) {
+          if (ch.e % a.share != 0) continue;
+          for (int e2 = ch.e; e2 < std::min(a.E, ch.e + a.share); ++e2)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              if (shj[j]) zbase[((int64_t)m * a.E + e2) * zstride + zcol[j]] = live[j] ? acc[j][q] : 0.0f;
+        } else {
+          if (!s_grp[r][1]) continue;
+          const int t = p / a.k, js = p % a.k;
+          for (uint32_t mask = (uint32_t)s_grp[r][0]; mask; mask &= mask - 1) {
+            const int j2 = __builtin_ctz(mask);
+            const int64_t r2 = j2 == js ? (int64_t)(ch.base + m) : (int64_t)a.pair_pos[t * a.k + j2];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              if (shj[j]) zbase[r2 * zstride + zcol[j]] = live[j] ? acc[j][q] : 0.0f;
+          }
+        }
+      } else {
+        // down: f V_G hn into the member's sub-row of the leader's row; the
+        // leader's row also gets the member mask
+        const int js = p % a.k;
+        const float f = __builtin_bit_cast(float, s_grp[r][3]);
+        float *dst = a.zsh + blockIdx.z * a.ks_stride_sh + ((int64_t)s_grp[r][2] * a.k + js) * a.Rsp;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (zcol[j] >= a.Rp) dst[zcol[j] - a.Rp] = live[j] ? acc[j][q] * f : 0.0f;
+        if (dl_writer && (lane & 15) == 0) a.dlead[ch.base + m] = s_grp[r][1] ? s_grp[r][0] : 0;
+      }
     }
   }
 }

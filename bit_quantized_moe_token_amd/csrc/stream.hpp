@@ -333,12 +333,36 @@ __device__ __forceinline__ void lut_store(const LutStage<Q> &ls, uint16_t *dst, 
   }
 }
 
-// z of the chunk's pairs in LDS: sums the ks fp32 partials of the
-// projection kernel (all loads issued before any add) and rounds to fp16;
-// with xk (gate/up) the sum is first scaled by 2^K of the row's token (z of
-// the normalised x~ = x 2^K).
+// Sum of the KS fp32 partials of four z columns (all loads issued before
+// the first add).
+__device__ __forceinline__ f32x4 zsum(const float *src, int64_t kstride, int KS) {
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= KS; k += 4) {
+    const f32x4 v0 = gld<f32x4>(src + (k + 0) * kstride), v1 = gld<f32x4>(src + (k + 1) * kstride);
+    const f32x4 v2 = gld<f32x4>(src + (k + 2) * kstride), v3 = gld<f32x4>(src + (k + 3) * kstride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum[i] += v0[i] + v1[i] + v2[i] + v3[i];
+  }
+  for (; k < KS; ++k) {
+    const f32x4 v = gld<f32x4>(src + k * kstride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum[i] += v[i];
+  }
+  return sum;
+}
+
+// z of the chunk's pairs in LDS, rounded to fp16: the sum of the ks fp32
+// partials of the projection kernel; zero for a pair outside its token's
+// leading n_comp slots and in the rank padding.
+//   gate/up (xk): scaled by 2^K of the row's token (z of the normalised
+//   x~ = x 2^K); rows by sorted position, or (z_tok) by (token, expert)
+//   (the group's leader has written the shared part into every member's
+//   row).
+//   down: the shared part is w' for the down leader of (token, group) —
+//   the sum of its members' sub-rows — and 0 for the other pairs.
 // zs layout: [NSUB*16 rows][width] fp16 with width = nset * RZ (RZ padded
-// columns per block); src column base = col0 within each partial row.
+// columns per block, the per-expert Rp first, then the shared Rsp).
 template <int NSUB, int NW>
 __device__ __forceinline__ void z_prologue(const FfnArgs &a, bool xk, const float *zpart, int zstride,
                                            int64_t kstride, int KS, int width, const Chunk &ch, uint16_t *zs) {
@@ -347,29 +371,41 @@ __device__ __forceinline__ void z_prologue(const FfnArgs &a, bool xk, const floa
   for (int o = tid; o < n4; o += NW * 64) {
     const int row = (4 * o) / width, col = (4 * o) % width;
     const int m = std::min(row, ch.cnt - 1);
-    // z rows by sorted position, or (z_tok, gate/up) by token and expert,
-    // zero for a pair outside the token's leading n_comp slots
     const int pr = a.sorted_pairs[ch.base + m];
     const int t = pr / a.k;
-    const bool by_tok = xk && a.z_tok;
-    const bool live = !by_tok || pr % a.k < a.n_comp;
-    const int K = xk ? a.xexp[t] : 0;
-    const float *src = zpart + (by_tok ? ((int64_t)t * a.E + ch.e) : (int64_t)(ch.base + m)) * zstride + col;
+    const bool shared = col % a.RZ >= a.Rp;
+    // rank padding (ranks are multiples of 8, so a float4 is padding or
+    // not as a whole) is zero and never read
+    const bool pad = shared ? col % a.RZ - a.Rp >= a.rs : col % a.RZ >= a.r;
+    const bool live = pr % a.k < a.n_comp && !pad;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    int k = 0;
-    for (; k + 4 <= KS; k += 4) {
-      const f32x4 v0 = gld<f32x4>(src + (k + 0) * kstride), v1 = gld<f32x4>(src + (k + 1) * kstride);
-      const f32x4 v2 = gld<f32x4>(src + (k + 2) * kstride), v3 = gld<f32x4>(src + (k + 3) * kstride);
+    if (live) {
+      if (shared && !xk) {
+        // the leader's own sub-row (read with its member mask, in one round
+        // trip), then the other members' (a group of several members is
+        // the rarer case)
+        const int pos = ch.base + m, js = pr % a.k;
+        const float *src = a.zsh + (int64_t)pos * a.k * a.Rsp + (col - a.Rp);
+        const uint32_t mask = (uint32_t)a.dlead[pos];
+        const f32x4 own = zsum(src + js * a.Rsp, a.ks_stride_sh, KS);
+        if (mask) {
+          sum = own;
+          for (uint32_t rest = mask & ~(1u << js); rest; rest &= rest - 1) {
+            const f32x4 v = zsum(src + __builtin_ctz(rest) * a.Rsp, a.ks_stride_sh, KS);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum[i] += v0[i] + v1[i] + v2[i] + v3[i];
+            for (int i = 0; i < 4; ++i) sum[i] += v[i];
+          }
+        }
+      } else {
+        const int64_t srow = (xk && a.z_tok) ? (int64_t)t * a.E + ch.e : (int64_t)(ch.base + m);
+        sum = zsum(zpart + srow * zstride + col, kstride, KS);
+        if (xk) {
+          const int K = a.xexp[t];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[i] = __builtin_ldexpf(sum[i], K);
+        }
+      }
     }
-    for (; k < KS; ++k) {
-      const f32x4 v = gld<f32x4>(src + k * kstride);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum[i] += v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sum[i] = live ? __builtin_ldexpf(sum[i], K) : 0.f;
     u32x2 h;
     h[0] = as_u32(f16x2{(f16)sum[0], (f16)sum[1]});
     h[1] = as_u32(f16x2{(f16)sum[2], (f16)sum[3]});
@@ -630,9 +666,11 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   Group<BG, PLANE> p0;
   Group<BU, PLANE> p1;
   preload_two<GPT, PLANE, BG, BU>(dg, du, strip, strip, 0, p0, p1);
-  // the rows' x exponents: requested now, kept in one register and put in
-  // LDS after the K walk (the epilogue reads them there)
-  const int kreg = threadIdx.x < NSUB * 16 ? row_kx(a, ch, threadIdx.x) : 0;
+  // the rows' pair ids and x exponents: requested now, kept in two
+  // registers and put in LDS after the K walk (the epilogue reads them
+  // there)
+  const int preg = threadIdx.x < NSUB * 16 ? a.sorted_pairs[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
+  const int kreg = threadIdx.x < NSUB * 16 ? a.xexp[preg / a.k] : 0;
   if (a.comp_on) {
     z_prologue<NSUB, 4>(a, true, a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
@@ -657,6 +695,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   // (the column sums' LDS is free once every wave has passed the barrier
   // below; the exponents go there)
   int *s_kx = reinterpret_cast<int *>(sx_region<NSUB, PLANE>(lds, a.RZ));
+  int *s_p = s_kx + NSUB * 16;
   if (a.comp_on) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -672,7 +711,10 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   // h 2^(kNormTop - eb) as fp16
   float *h32 = reinterpret_cast<float *>(lds);
   __syncthreads();
-  if (threadIdx.x < NSUB * 16) s_kx[threadIdx.x] = kreg;
+  if (threadIdx.x < NSUB * 16) {
+    s_kx[threadIdx.x] = kreg;
+    s_p[threadIdx.x] = preg;
+  }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -704,7 +746,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
       *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + m) * a.I + 64 * sg + c8) = o;
       if ((tid & 7) == 0) {
         a.hblk[(int64_t)(ch.base + m) * a.hblk_stride + sg] = (int8_t)eb;
-        h_pair_exp(a, ch.base + m, eb);
+        h_pair_exp(a, ch.base + m, s_p[m], eb);
       }
     }
   }

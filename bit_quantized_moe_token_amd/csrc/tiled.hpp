@@ -89,8 +89,9 @@ constexpr int kTMetaBytes = 4 * 512;                  // per wave: 64 lanes x 2 
 constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
 constexpr int kTStages = 3;
 constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
-// dynamic LDS of a tiled launch: the stages, then the gate/up rows' x exponents
-constexpr size_t kTiledLdsLaunch = kTiledLdsBytes + kTM * 4;
+// dynamic LDS of a tiled launch: the stages, then the gate/up rows' x
+// exponents and pair ids
+constexpr size_t kTiledLdsLaunch = kTiledLdsBytes + 2 * kTM * 4;
 
 // DMA operations per strip per tile: one 16-byte transfer for 4-bit codes,
 // else one 4-byte transfer per code dword.
@@ -263,7 +264,8 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   }
   // the rows' x exponents: requested now, stored past the LDS stages after
   // the K walk (so that nothing waits for them)
-  const int kreg = threadIdx.x < kTM ? row_kx(a, ch, threadIdx.x) : 0;
+  const int preg = threadIdx.x < kTM ? a.sorted_pairs[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
+  const int kreg = threadIdx.x < kTM ? a.xexp[preg / a.k] : 0;
   f32x4 acc[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -283,7 +285,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   // partial, and the first U operands) are requested before the K walk, so
   // the epilogue does not wait for memory
   const int zw = 2 * a.RZ;
-  const bool zpre = a.comp_on && a.ks_gu == 1 && zw <= 64;
+  const bool zpre = a.comp_on && a.ks_gu == 1 && zw <= 64 && a.rs == 0;
   ZPre<8, 4, 8> zp;
   if (zpre) z_preload<8, 4, 8>(a.zp_gu, zw, zw, ch, zp);
   f16x8 ub[4];
@@ -294,7 +296,11 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   kl.template run<8>(acc);
   // acc holds W x~ (x~ = x 2^K, the normalised rows), as do the z rows
   int *s_kx = reinterpret_cast<int *>(lds + kTiledLdsBytes);
-  if (threadIdx.x < kTM) s_kx[threadIdx.x] = kreg;
+  int *s_p = s_kx + kTM;
+  if (threadIdx.x < kTM) {
+    s_kx[threadIdx.x] = kreg;
+    s_p[threadIdx.x] = preg;
+  }
   __syncthreads();
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
@@ -351,7 +357,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
       }
       *reinterpret_cast<u32x4 *>(a.h + (int64_t)(ch.base + r) * a.I + nt * kTileK + c8) = o;
       if ((tid & 15) < 2) a.hblk[(int64_t)(ch.base + r) * a.hblk_stride + 2 * nt + (tid & 15)] = (int8_t)eb;
-      if ((tid & 15) == 0) h_pair_exp(a, ch.base + r, eb);
+      if ((tid & 15) == 0) h_pair_exp(a, ch.base + r, s_p[r], eb);
     }
   }
 }

@@ -13,10 +13,12 @@ key, so that changing T (or drawing fewer rows) never shifts any other draw:
   [seed, 7, grp, blk, 0|1]       shared compensator factors U | V, N(0, 0.01)
   [seed, 8, e, blk]              Gaussian test matrix of the compensator fit, N(0, 1)
 
-"N(0, s)" is read as mean 0 and standard deviation s.  Two optional config
-keys move a layer across the fp16 range without changing any draw: x_scale
-multiplies the activations and w_scale the expert weights (both before the
-rounding to fp16).  Blocks are numbered
+"N(0, s)" is read as mean 0 and standard deviation s.  Optional config keys
+change a layer without changing any draw: x_scale multiplies the activations
+and w_scale the expert weights (both move a layer across the fp16 range),
+and factor_std replaces the 0.01 of the random compensator factors (larger
+values make the low-rank terms a large part of the output); each is applied
+before the rounding to fp16.  Blocks are numbered
 0 = gate, 1 = up, 2 = down; gate/up blocks are [I, H] (rows = outputs), down
 is [H, I].  Values are rounded to the storage type (fp16 weights, activations
 and factors, fp32 logits) here, and those rounded values are the inputs of
@@ -147,8 +149,9 @@ def gen_factors(cfg, seed, e, blk):
     if r == 0:
         return None
     n, kdim = block_shape(cfg, blk)
-    U = (_rng(seed, 4, e, blk, 0).standard_normal((n, r)) * 0.01).astype(np.float16)
-    V = (_rng(seed, 4, e, blk, 1).standard_normal((r, kdim)) * 0.01).astype(np.float16)
+    sd = cfg.get("factor_std", 0.01)
+    U = (_rng(seed, 4, e, blk, 0).standard_normal((n, r)) * sd).astype(np.float16)
+    V = (_rng(seed, 4, e, blk, 1).standard_normal((r, kdim)) * sd).astype(np.float16)
     return U, V
 
 
@@ -158,8 +161,9 @@ def gen_shared_factors(cfg, seed, grp, blk):
     if rs == 0:
         return None
     n, kdim = block_shape(cfg, blk)
-    U = (_rng(seed, 7, grp, blk, 0).standard_normal((n, rs)) * 0.01).astype(np.float16)
-    V = (_rng(seed, 7, grp, blk, 1).standard_normal((rs, kdim)) * 0.01).astype(np.float16)
+    sd = cfg.get("factor_std", 0.01)
+    U = (_rng(seed, 7, grp, blk, 0).standard_normal((n, rs)) * sd).astype(np.float16)
+    V = (_rng(seed, 7, grp, blk, 1).standard_normal((rs, kdim)) * sd).astype(np.float16)
     return U, V
 
 

@@ -27,6 +27,11 @@ CASES = {
     # lookup over four 64-lane passes, routing with E = 256
     "many_experts": ("finegrained", dict(E=256, k=8, T=48, H=256, I=256)),
     "many_experts_bitplane": ("bitplane", dict(E=256, T=40, H=256, I=256)),
+    # shared factors on an INT layer (groups of 4 of 16 experts, so a
+    # token's six experts often share groups) whose low-rank terms are a
+    # large part of the output (factors N(0, 0.05)); two of six slots
+    # compensated, so the groups' leaders come from those slots only
+    "shared_int": ("finegrained", dict(E=16, T=64, H=512, I=1408, rs=32, share=4, factor_std=0.05)),
 }
 
 _cache = {}
@@ -71,7 +76,7 @@ def test_ffn_matches_oracle(case, seed):
     layers.check_y(y16.float().cpu().numpy(), ref, f"{case} seed {seed} fp16")
 
 
-@pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane"])
+@pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane", "shared_int"])
 def test_ffn_compensation_switch(case):
     """n_comp in {0, 1, k} against the oracle; n_comp = 0 equals the layer
     without factors bit for bit."""
@@ -155,7 +160,7 @@ def test_ffn_zero_input_and_few_tokens():
 # including one token tile per expert (decode), mixed 2/3/4-bit blocks with
 # group 64 and an odd, ragged K-tile count (fine-grained: I = 1408 = 11 tiles)
 
-@pytest.mark.parametrize("case", ["tiny", "decode", "prefill", "finegrained"])
+@pytest.mark.parametrize("case", ["tiny", "decode", "prefill", "finegrained", "shared_int"])
 def test_ffn_tiled_path_matches_oracle(case):
     cfg, orc, dev, x, logits = _setup(case)
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])

@@ -19,6 +19,8 @@ CASES = {
     "decode_t1": ("decode", dict(H=512, I=1792, T=1)),    # fused, one token
     "tiny_t64": ("tiny", {}),                             # more than 16 tokens: route, then FFN
     "finegrained": ("finegrained", dict(T=16)),           # E 64 > 4 k: route, then FFN
+    # fused, with shared factors (groups of 2) large in the output
+    "tiny_shared": ("tiny", dict(T=16, rs=16, share=2, factor_std=0.05)),
 }
 _cache = {}
 
