@@ -632,13 +632,21 @@ __device__ __forceinline__ void row_ptrs(const uint16_t **rowp, const FfnArgs &a
 // LDS layout of both stream kernels: [x staging | z rows (2 RZ columns) |
 // per-group column sums (4 tiles x 2 groups x NSUB*16 rows, fp32) | per wave:
 // its two streams' bit-plane LUTs (bit-plane kernels only)].  The gate/up
-// epilogue reuses the staging area for its fp32 h tile.
+// epilogue reuses the staging area for its fp32 h tile.  The bit-plane
+// kernels build their z rows after the K walk, in the staging area: their
+// LUTs already hold them near the LDS limit, and the 8 KiB this saves make
+// room for a third workgroup per CU.
+template <bool PLANE>
+__host__ __device__ constexpr bool z_late() { return PLANE; }
+static_assert(2 * (64 + 64) <= kXStride, "z rows of the largest ranks fit a staged activation row");
+
 template <int NSUB, bool PLANE>
-__device__ __forceinline__ int zs_offset() { return xs_bufs<NSUB, PLANE>() * xs_halves<NSUB>(); }
+__device__ __forceinline__ int zs_offset() { return z_late<PLANE>() ? 0 : xs_bufs<NSUB, PLANE>() * xs_halves<NSUB>(); }
 
 template <int NSUB, bool PLANE>
 __device__ __forceinline__ float *sx_region(uint16_t *lds, int RZ) {
-  return reinterpret_cast<float *>(lds + zs_offset<NSUB, PLANE>() + NSUB * 16 * 2 * RZ);
+  return reinterpret_cast<float *>(lds + xs_bufs<NSUB, PLANE>() * xs_halves<NSUB>() +
+                                   (z_late<PLANE>() ? 0 : NSUB * 16 * 2 * RZ));
 }
 
 template <int NSUB, bool PLANE>
@@ -671,7 +679,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   // there)
   const int preg = threadIdx.x < NSUB * 16 ? a.sorted_pairs[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
   const int kreg = threadIdx.x < NSUB * 16 ? a.xexp[preg / a.k] : 0;
-  if (a.comp_on) {
+  if (!z_late<PLANE>() && a.comp_on) {
     z_prologue<NSUB, 4>(a, true, a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
   }
@@ -696,6 +704,11 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, const Chunk &ch, i
   // below; the exponents go there)
   int *s_kx = reinterpret_cast<int *>(sx_region<NSUB, PLANE>(lds, a.RZ));
   int *s_p = s_kx + NSUB * 16;
+  if (z_late<PLANE>() && a.comp_on) {
+    __syncthreads();     // every wave is done with the staging area
+    z_prologue<NSUB, 4>(a, true, a.zp_gu, 2 * a.RZ, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    __syncthreads();
+  }
   if (a.comp_on) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -769,7 +782,7 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   const int st0 = 8 * sg + 2 * wave, st1 = st0 + 1;
   Group<BD, PLANE> p0, p1;
   if (g1 > g0) preload_two<GPT, PLANE, BD, BD>(d, d, st0, st1, g0, p0, p1);
-  if (epi) {
+  if (!z_late<PLANE>() && epi) {
     z_prologue<NSUB, 4>(a, false, a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, zw, ch, zs);
     __syncthreads();
   }
@@ -789,6 +802,11 @@ __device__ __forceinline__ void down_body(const FfnArgs &a, const Chunk &ch, int
   if (g1 > g0)
     stream_two<NSUB, 4, GPT, PLANE, BD, BD>(d, d, st0, st1, g0, g1, rowp, xs, sx_region<NSUB, PLANE>(lds, a.RZ),
                                             lut_region<NSUB, PLANE>(lds, a.RZ, wave), acc, p0, p1);
+  if (z_late<PLANE>() && epi) {
+    __syncthreads();     // every wave is done with the staging area
+    z_prologue<NSUB, 4>(a, false, a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, zw, ch, zs);
+    __syncthreads();
+  }
   float *yp = a.ypart + (int64_t)split * a.P * a.H;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -818,10 +836,11 @@ __device__ __forceinline__ uint16_t *dyn_lds() {
 // costs less than their idle MFMA rows).  One launch per call.
 __device__ __forceinline__ int chunk_class(int nsub_max) { return nsub_max == 1 ? 1 : 2; }
 
-// LDS bytes of one class: x staging, z rows, column sums, per-wave LUTs.
+// LDS bytes of one class: x staging, z rows (in the staging area for the
+// bit-plane kernels), column sums, per-wave LUTs.
 inline size_t stream_lds_bytes(bool plane, int nsub, int RZ) {
   const size_t nb = plane ? 1 : (nsub == 1 ? xs_bufs<1, false>() : 1);
-  return nb * nsub * 16 * kXStride * 2 + (size_t)nsub * 16 * 2 * RZ * 2 + nb * 8 * nsub * 16 * 4 +
+  return nb * nsub * 16 * kXStride * 2 + (plane ? 0 : (size_t)nsub * 16 * 2 * RZ * 2) + nb * 8 * nsub * 16 * 4 +
          (plane ? (size_t)4 * 2 * kLutBlk * 2 : 0);
 }
 
