@@ -169,39 +169,72 @@ __device__ __forceinline__ float down_key(float g, int eh) {
   return g > 0.f ? (float)eh + __builtin_log2f(g) : -__builtin_inff();
 }
 
+// Eight slots j0 .. j0 + 7 of a token (row = t * k) as loaded, every load
+// issued before the first use (all indexed by pair id, so none waits for
+// another): the experts, and for DOWN the positions, gates and h exponents.
+struct SlotBatch {
+  int id[8], pp[8], eh[8];
+  float g[8];
+};
+
+// (the loads are unconditional, at slots clamped to n_comp - 1 >= 0, so
+// that no branch separates them and nothing uses them before the fold;
+// the fold skips the slots past n_comp)
 template <bool DOWN>
-__device__ __forceinline__ SlotGroup slot_group(const FfnArgs &a, int t, int G) {
-  SlotGroup g{0u, -1, 0, -__builtin_inff()};
-  const int64_t row = (int64_t)t * a.k;
-  for (int j0 = 0; j0 < a.n_comp; j0 += 8) {
-    // a batch of eight slots: every load issued before the first use (all
-    // indexed by pair id, so none waits for another)
-    int id[8], pp[8], eh[8];
-    float gv[8];
+__device__ __forceinline__ void slot_batch_load(const FfnArgs &a, int64_t row, int j0, SlotBatch &b) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = j0 + u < a.n_comp;
-      id[u] = ok ? a.ids[row + j0 + u] : -1;
-      pp[u] = (DOWN && ok) ? a.pair_pos[row + j0 + u] : 0;
-      gv[u] = (DOWN && ok) ? a.gates[row + j0 + u] : 0.f;
+  for (int u = 0; u < 8; ++u) {
+    const int64_t q = row + std::min(j0 + u, a.n_comp - 1);
+    b.id[u] = a.ids[q];
+    if (DOWN) {
+      b.pp[u] = a.pair_pos[q];
+      b.g[u] = a.gates[q];
+      b.eh[u] = a.hexpf[q];
+    } else {
+      b.pp[u] = 0;
+      b.g[u] = 0.f;
+      b.eh[u] = 0;
     }
+  }
+}
+
+template <bool DOWN>
+__device__ __forceinline__ void slot_batch_fold(const FfnArgs &a, int j0, int G, SlotBatch b, SlotGroup &g) {
+  // (the values pass through an empty asm here, so that the compiler does
+  // not move their uses, and the wait for the loads, up to where they were
+  // requested)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) eh[u] = (DOWN && j0 + u < a.n_comp) ? a.hexpf[row + j0 + u] : 0;
+  for (int u = 0; u < 8; ++u) {
+    asm volatile("" : "+v"(b.id[u]), "+v"(b.pp[u]), "+v"(b.g[u]), "+v"(b.eh[u]));
+  }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (id[u] < 0 || id[u] / a.share != G) continue;
-      g.mask |= 1u << (j0 + u);
-      if (!DOWN) {
-        if (g.lead < 0) g.lead = j0 + u;
-      } else {
-        const float key = down_key(gv[u], eh[u]);
-        if (g.lead < 0 || key > g.key) {
-          g.key = key;
-          g.lead = j0 + u;
-          g.lead_pos = pp[u];
-        }
+  for (int u = 0; u < 8; ++u) {
+    if (j0 + u >= a.n_comp || b.id[u] / a.share != G) continue;
+    g.mask |= 1u << (j0 + u);
+    if (!DOWN) {
+      if (g.lead < 0) g.lead = j0 + u;
+    } else {
+      const float key = down_key(b.g[u], b.eh[u]);
+      if (g.lead < 0 || key > g.key) {
+        g.key = key;
+        g.lead = j0 + u;
+        g.lead_pos = b.pp[u];
       }
     }
+  }
+}
+
+// The group of (t, G), from slots 0..7 loaded earlier (first) and the
+// rest loaded here.
+template <bool DOWN>
+__device__ __forceinline__ SlotGroup slot_group_from(const FfnArgs &a, int t, int G, const SlotBatch &first) {
+  SlotGroup g{0u, -1, 0, -__builtin_inff()};
+  slot_batch_fold<DOWN>(a, 0, G, first, g);
+  const int64_t row = (int64_t)t * a.k;
+  for (int j0 = 8; j0 < a.n_comp; j0 += 8) {
+    SlotBatch b;
+    slot_batch_load<DOWN>(a, row, j0, b);
+    slot_batch_fold<DOWN>(a, j0, G, b, g);
   }
   return g;
 }

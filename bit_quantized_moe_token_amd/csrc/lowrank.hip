@@ -32,7 +32,9 @@ namespace moeq {
 // (token, expert) pair needs no routing, so both fit in one launch.
 // A tile none of whose pairs is compensated (router-guided top-n) loads
 // no V and writes zero rows.
-template <int NJ, bool ROUTE>
+// SH: the layer has shared factors (the group bookkeeping is compiled in
+// only then: its registers would cost the other layers occupancy).
+template <int NJ, bool ROUTE, bool SH>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy, RouteOut ro) {
   __shared__ f32x4 s_part[4][NJ][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -72,26 +74,24 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   const bool gu = mode != 1;
   // shared factors (see slot_group): the group of the lane's row — its
   // member mask, whether the row leads it and (mode 1) the leader's
-  // position and the row's factor f — requested now and handed to the
-  // store phase through LDS after the main loop.  Gate/up: V_G x is
-  // computed for every row of a tile; only the leader of each (token,
-  // group) stores it, into the rows of all members (mode 2: the group's
-  // first expert, for the group's experts).
-  int gmask = 0, glead = 0, gpos = 0;
-  float gf = 0.f;
-  if (a.rs > 0 && !tok && comp_row) {
-    const int p = a.sorted_pairs[pos];
-    const int t = p / a.k, j = p % a.k;
+  // position and the row's factor f.  The token's first eight slots are
+  // requested now (with the row's own gate and h exponent), folded after
+  // the main loop and handed to the store phase through LDS.  Gate/up:
+  // V_G x is computed for every row of a tile; only the leader of each
+  // (token, group) stores it, into the rows of all members (mode 2: the
+  // group's first expert, for the group's experts).
+  const bool grp = SH && !tok && comp_row;
+  SlotBatch sb;
+  float g_own = 0.f;
+  int eh_own = 0, p_own = 0;
+  if (grp) {
+    p_own = a.sorted_pairs[pos];
     if (gu) {
-      const SlotGroup sg = slot_group<false>(a, t, ch.e / a.share);
-      gmask = (int)sg.mask;
-      glead = sg.lead == j;
+      slot_batch_load<false>(a, (int64_t)(p_own / a.k) * a.k, 0, sb);
     } else {
-      const SlotGroup sg = slot_group<true>(a, t, ch.e / a.share);
-      gmask = (int)sg.mask;
-      glead = sg.lead == j;
-      gpos = sg.lead_pos;
-      gf = down_factor(down_key(a.gates[p], a.hexpf[p]), sg.key);
+      slot_batch_load<true>(a, (int64_t)(p_own / a.k) * a.k, 0, sb);
+      g_own = a.gates[p_own];
+      eh_own = a.hexpf[p_own];
     }
   }
   // mode 1: y slice 0 writes hn
@@ -234,6 +234,22 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   for (int j = 0; j < NJ; ++j) s_part[wave][j][lane] = acc[j];
   __shared__ int s_grp[16][4];
   if (wave == 0 && lane < 16) {
+    int gmask = 0, glead = 0, gpos = 0;
+    float gf = 0.f;
+    if (grp) {
+      const int t = p_own / a.k, j = p_own % a.k;
+      if (gu) {
+        const SlotGroup sg = slot_group_from<false>(a, t, ch.e / a.share, sb);
+        gmask = (int)sg.mask;
+        glead = sg.lead == j;
+      } else {
+        const SlotGroup sg = slot_group_from<true>(a, t, ch.e / a.share, sb);
+        gmask = (int)sg.mask;
+        glead = sg.lead == j;
+        gpos = sg.lead_pos;
+        gf = down_factor(down_key(g_own, eh_own), sg.key);
+      }
+    }
     s_grp[lane][0] = gmask;
     s_grp[lane][1] = glead;
     s_grp[lane][2] = gpos;
@@ -272,7 +288,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
       for (int j = 0; j < NJ; ++j)
         if (!shj[j] && !(mode == 1 && zcol[j] >= a.Rp))
           zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
-      if (!any_sh || !comp) continue;
+      if (!any_sh || !comp || (!SH && !tok)) continue;
       const int r = m - 16 * sub;
       if (gu) {
         // the leader writes V_G x into the row of every member of its group
@@ -385,11 +401,20 @@ void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s)
   const int njy = (int)grid.y;
   if (mode != 1) grid.y += 1;                 // the x-exponent slice
   const RouteOut ro{};
-  switch (nj) {
-    case 8: hipLaunchKernelGGL((lowrank_project_kernel<8, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
-    case 4: hipLaunchKernelGGL((lowrank_project_kernel<4, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
-    case 2: hipLaunchKernelGGL((lowrank_project_kernel<2, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
-    default: hipLaunchKernelGGL((lowrank_project_kernel<1, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+  if (a.rs > 0) {
+    switch (nj) {
+      case 8: hipLaunchKernelGGL((lowrank_project_kernel<8, false, true>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      case 4: hipLaunchKernelGGL((lowrank_project_kernel<4, false, true>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      case 2: hipLaunchKernelGGL((lowrank_project_kernel<2, false, true>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      default: hipLaunchKernelGGL((lowrank_project_kernel<1, false, true>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+    }
+  } else {
+    switch (nj) {
+      case 8: hipLaunchKernelGGL((lowrank_project_kernel<8, false, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      case 4: hipLaunchKernelGGL((lowrank_project_kernel<4, false, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      case 2: hipLaunchKernelGGL((lowrank_project_kernel<2, false, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+      default: hipLaunchKernelGGL((lowrank_project_kernel<1, false, false>), grid, dim3(256), 0, s, a, mode, njy, ro); break;
+    }
   }
 }
 
@@ -399,7 +424,8 @@ void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s)
 void launch_front_routed(const FfnArgs &a, const RouteOut &ro, hipStream_t s) {
   const int njy = a.comp_on ? 2 * a.RZ / 16 : 0;
   const dim3 grid(a.comp_on ? (a.T + 15) / 16 * a.E : (a.T + 3) / 4, njy + 2, a.comp_on ? a.ks_gu : 1);
-  hipLaunchKernelGGL((lowrank_project_kernel<1, true>), grid, dim3(256), 0, s, a, 2, njy, ro);
+  // (mode 2 stores shared columns without the group bookkeeping)
+  hipLaunchKernelGGL((lowrank_project_kernel<1, true, false>), grid, dim3(256), 0, s, a, 2, njy, ro);
 }
 
 // x exponents when no gate/up projection runs: one wave per token.
