@@ -31,15 +31,23 @@ static bool tiled_fits(const moeq_layer *L, int T, int k) {
          (int64_t)T * D.H < (1ll << 31) && P * D.I < (1ll << 31) && 2 * RZ <= kTileK + 8;
 }
 
-// Average pairs per expert from which the tiled path is faster, measured on
-// the Mixtral-sized layer (E = 8, k = 2): about 96 for int4 (T = 384) and
-// 384 for int3 (T = 1536), whose fields cost the tiled decode more; layers
-// with any block below 4 bits take the larger figure.
+// Average pairs per expert from which the tiled path is faster: about 96
+// for int4, measured on the Mixtral-sized layer (E = 8, k = 2, I = 14336:
+// T = 384) and on the fine-grained one (E = 64, k = 6, I = 1408: T = 1024);
+// 384 for int3 on the Mixtral-sized layer (T = 1536), whose fields cost the
+// tiled decode more; layers with any block below 4 bits take the larger
+// figure.
 static int64_t tiled_min_pairs(const moeq_layer *L) {
   for (uint8_t b : L->bits)
     if (b != 4) return 384;
   return 96;
 }
+
+// Fewest gate/up workgroups (token tiles x 128-row tiles of I) for which the
+// tiled path is taken: below one per CU its grid leaves the chip idle (the
+// 8-expert layer with H = 256, I = 512 streams faster at every batch up to
+// 384 pairs per expert, where its tiled grid has 124 workgroups).
+constexpr int64_t kTiledMinGrid = 256;
 
 static int pick_path(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {
   const int want = o ? o->path : MOEQ_PATH_AUTO;
@@ -47,7 +55,9 @@ static int pick_path(const moeq_layer *L, int T, int k, const moeq_ffn_options *
   if (want == MOEQ_PATH_STREAM) return MOEQ_PATH_STREAM;
   if (want != MOEQ_PATH_AUTO) return -1;
   const int64_t P = (int64_t)T * k;
-  return (tiled_fits(L, T, k) && P >= tiled_min_pairs(L) * L->dims.E) ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
+  const int64_t grid = (int64_t)max_chunks(L->dims.E, T, k, kTiledM) * (L->dims.I / kTileK);
+  return (tiled_fits(L, T, k) && P >= tiled_min_pairs(L) * L->dims.E && grid >= kTiledMinGrid)
+             ? MOEQ_PATH_TILED : MOEQ_PATH_STREAM;
 }
 
 static int pick_splits(const moeq_layer *L, int T, int k, const moeq_ffn_options *o) {

@@ -213,6 +213,39 @@ def test_ffn_default_path_int3():
     assert torch.equal(auto_s, stream_s)
 
 
+def _gateup_kernel_run(dev, cfg, x, logits):
+    """Name of the gate/up kernel the default path launches."""
+    from bit_quantized_moe_token_amd import moeq
+    moeq.profile_enable(True)
+    try:
+        _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+        names = set(moeq.profile_read())
+    finally:
+        moeq.profile_enable(False)
+    gu = sorted(n for n in names if n.startswith("gateup"))
+    assert len(gu) == 1, names
+    return gu[0]
+
+
+def test_default_path_boundary():
+    """The default path turns tiled at an average of exactly 96 pairs per
+    expert on an int4 layer whose tiled grid is large enough (E = 8, k = 2,
+    I = 3584: T = 384 tiles, T = 380 streams), and a layer whose tiled grid
+    would leave most CUs idle (H = 256, I = 512, 124 workgroups at 384 pairs
+    per expert) streams at any batch."""
+    cfg = configs.reduced(configs.get("prefill"), H=512, I=3584, T=384)
+    dev = layers.device_layer(cfg, 0)
+    x, logits = gen.gen_x(cfg, 0), gen.gen_logits(cfg, 0)
+    assert cfg["T"] * cfg["k"] == 96 * cfg["E"]
+    assert _gateup_kernel_run(dev, cfg, x, logits) == "gateup_tiled"
+    c95 = dict(cfg, T=380)
+    assert _gateup_kernel_run(dev, c95, x[:380].copy(), logits[:380].copy()) == "gateup_stream"
+    del dev
+    tiny = configs.reduced(configs.get("tiny"), T=1536)
+    dev = layers.device_layer(tiny, 0, layers.oracle_layer(tiny, 0, cache_blocks=3 * tiny["E"]))
+    assert _gateup_kernel_run(dev, tiny, gen.gen_x(tiny, 0), gen.gen_logits(tiny, 0)) == "gateup_stream"
+
+
 def test_ffn_tiled_unsupported_for_bitplane():
     from bit_quantized_moe_token_amd import moeq
     cfg, orc, dev, x, logits = _setup("bitplane")
