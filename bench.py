@@ -281,6 +281,23 @@ KERNEL_KEYS = [("gateup_kernel", "gateup_stream"), ("down_kernel", "down_stream"
                ("route", "route"), ("combine", "combine"), ("neg_kernel", "calibration_copy")]
 
 
+def route_scaling(reps=20):
+    """moeq_route alone on seeded N(0, 1) logits, 128 experts, top-8, at
+    batches from 512 to 32768 tokens: beyond 4096 tokens the sort counts
+    through a workspace, so its time should grow about linearly."""
+    import numpy as np
+    import torch
+    from bit_quantized_moe_token_amd import moeq
+    res = []
+    for T in (512, 4096, 8192, 32768):
+        logits = torch.from_numpy(np.random.default_rng([0, T]).standard_normal((T, 128)).astype(np.float32)).cuda()
+        rt = moeq.RoutingOut(T, 128, 8, logits.device)
+        ms = time_steps(lambda i: moeq.route(logits, 8, out=rt), reps, 3)
+        res.append(dict(T=T, us=ms * 1e3))
+        del logits, rt
+    return dict(E=128, k=8, what="moeq_route, mean of %d calls" % reps, batches=res)
+
+
 def hbm_context(reps=10):
     """Plain torch streaming kernels over 1 GiB (a read-only sum and a copy),
     timed with events on torch's stream: what simple streaming code reaches
@@ -608,6 +625,7 @@ def main():
             torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_extra:
         out["hbm_context"] = hbm_context()
+        out["route_scaling"] = route_scaling()
     if not args.no_cpu_baseline:
         # decode: the whole 16-token batch, repeated for about 12 s
         out["cpu_baseline"] = cpu_baseline(cfg, args.seed, min(cfg["T"], 16))

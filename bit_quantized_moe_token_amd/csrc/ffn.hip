@@ -261,11 +261,19 @@ MOEQ_API moeq_status moeq_expert_ffn(const moeq_layer *L, const uint16_t *x, int
   return ffn_rest(a, path, y, y_dtype, stream);
 }
 
+// Unfused calls: the FFN's workspace, then (long batches) the routing's.
 MOEQ_API moeq_status moeq_forward_workspace_size(const moeq_layer *L, int32_t T, int32_t k,
                                                  const moeq_ffn_options *opts, size_t *bytes) {
   moeq_status st = moeq_ffn_workspace_size(L, T, k, opts, bytes);
   if (st != MOEQ_OK) return st;
-  if (fusable(L, T, k, opts)) *bytes = ws_plan(L, T, k, pick_splits(L, T, k, opts), true).total;
+  if (fusable(L, T, k, opts)) {
+    *bytes = ws_plan(L, T, k, pick_splits(L, T, k, opts), true).total;
+  } else {
+    size_t rb = 0;
+    st = moeq_route_workspace_size(T, L->dims.E, k, &rb);
+    if (st != MOEQ_OK) return st;
+    if (rb) *bytes = al256(*bytes) + rb;
+  }
   return MOEQ_OK;
 }
 
@@ -274,8 +282,20 @@ MOEQ_API moeq_status moeq_moe_forward(const moeq_layer *L, const float *logits, 
                                       void *ws, size_t ws_bytes, const moeq_ffn_options *opts, hipStream_t stream) {
   if (!L || !r) return fail(MOEQ_ERR_INVALID, "moe_forward: null layer or routing");
   if (!fusable(L, T, k, opts)) {
-    // routing, then the expert FFN (the FFN's workspace is the whole ws)
-    moeq_status st = moeq_route(logits, T, L->dims.E, k, r, nullptr, 0, stream);
+    // routing (into the end of ws when it needs a workspace), then the
+    // expert FFN
+    size_t fb = 0, rb = 0;
+    moeq_status st = moeq_ffn_workspace_size(L, T, k, opts, &fb);
+    if (st != MOEQ_OK) return st;
+    st = moeq_route_workspace_size(T, L->dims.E, k, &rb);
+    if (st != MOEQ_OK) return st;
+    void *rws = nullptr;
+    if (rb) {
+      if (!ws || ws_bytes < al256(fb) + rb)
+        return fail(MOEQ_ERR_WORKSPACE, "moe_forward: workspace has %zu bytes, needs %zu", ws_bytes, al256(fb) + rb);
+      rws = static_cast<uint8_t *>(ws) + al256(fb);
+    }
+    st = moeq_route(logits, T, L->dims.E, k, r, rws, rb, stream);
     if (st != MOEQ_OK) return st;
     return moeq_expert_ffn(L, x, T, k, r, n_comp, y, y_dtype, ws, ws_bytes, opts, stream);
   }

@@ -1,7 +1,9 @@
 // Top-k routing and the token -> expert counting sort: in one workgroup for
 // up to 16 tokens; else top-k in workgroups of 4 tokens, then placement in
-// 64-token segments (each segment counts every pair's expert itself, so
-// no workspace and no grid-wide step are needed).
+// 64-token segments.  Up to 4096 tokens each segment counts every pair's
+// expert itself (no workspace, no grid-wide step); beyond, per-segment
+// histograms and one scan over the segments go through a workspace, so the
+// work stays linear in the batch.
 //
 // Top-k with softmax gates over the selected logits (router-guided top-n
 // compensation, "Bandwidth-Efficient Adaptive Mixture-of-Experts via
@@ -42,25 +44,12 @@ route_topk_kernel(const float *__restrict__ logits, int T, int E, int k, int32_t
   topk_tokens<1>(logits, t, T, kTopkWaves, E, k, ids, gates, nullptr);
 }
 
-// Segment blockIdx.x: per-expert pair totals and the counts of the pairs
-// before the segment, from all T*k expert ids (LDS counters); expert
-// offsets by an exclusive scan (segment 0 writes them); then the stable
-// placement of the segment's pairs in ascending pair id (ballot peer masks
-// inside a wave, per-wave counts across waves and chunks).
-__global__ void __launch_bounds__(kSegThreads)
-route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
-                   int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ pair_pos) {
-  __shared__ int s_tot[kMaxE];
-  __shared__ int s_base[kMaxE];
-  __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_run[kMaxE];
-  __shared__ int s_wave[kSegWaves][kMaxE];
+// Per-expert totals (s_tot) and counts of the pairs before p0 (s_base) of
+// all P expert ids, then the offsets (s_off) by an exclusive scan; every
+// thread of the workgroup takes part.
+__device__ __forceinline__ void count_before(const int32_t *__restrict__ ids, int P, int p0, int E, int *s_tot,
+                                             int *s_base, int *s_off) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seg = blockIdx.x;
-  const int P = T * k;
-  const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
-  for (int e = tid; e < E; e += kSegThreads) { s_tot[e] = 0; s_base[e] = 0; s_run[e] = 0; }
-  __syncthreads();
   // ids in batches of 16 per thread: a batch's loads are all requested
   // before its first counter update, so it waits for memory once
   constexpr int kCountBatch = 16;
@@ -98,10 +87,40 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t
     if (lane == 0) s_off[E] = carry;
   }
   __syncthreads();
-  if (seg == 0)
-    for (int e = tid; e <= E; e += kSegThreads) offsets[e] = s_off[e];
-  for (int e = tid; e < E; e += kSegThreads) s_base[e] += s_off[e];
-  __syncthreads();
+}
+
+// Segment blockIdx.x: per-expert pair totals and the counts of the pairs
+// before the segment, from all T*k expert ids (LDS counters); expert
+// offsets by an exclusive scan (segment 0 writes them); then the stable
+// placement of the segment's pairs in ascending pair id (ballot peer masks
+// inside a wave, per-wave counts across waves and chunks).
+// seg_base (long batches, see route_scan_kernel): the segment's first
+// position per expert, computed beforehand; the kernel then only places.
+__global__ void __launch_bounds__(kSegThreads)
+route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
+                   int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ pair_pos,
+                   const int32_t *__restrict__ seg_base) {
+  __shared__ int s_tot[kMaxE];
+  __shared__ int s_base[kMaxE];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_run[kMaxE];
+  __shared__ int s_wave[kSegWaves][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = blockIdx.x;
+  const int P = T * k;
+  const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
+  for (int e = tid; e < E; e += kSegThreads) { s_tot[e] = 0; s_base[e] = 0; s_run[e] = 0; }
+  if (seg_base) {
+    for (int e = tid; e < E; e += kSegThreads) s_base[e] = seg_base[(int64_t)seg * E + e];
+    __syncthreads();
+  } else {
+    __syncthreads();
+    count_before(ids, P, p0, E, s_tot, s_base, s_off);
+    if (seg == 0)
+      for (int e = tid; e <= E; e += kSegThreads) offsets[e] = s_off[e];
+    for (int e = tid; e < E; e += kSegThreads) s_base[e] += s_off[e];
+    __syncthreads();
+  }
   for (int base = p0; base < p1; base += kSegThreads) {
     const int p = base + tid;
     const bool valid = p < p1;
@@ -137,6 +156,75 @@ route_place_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t
 }
 
 static inline int route_segments(int T) { return (T + kSegTokens - 1) / kSegTokens; }
+
+// ---- long batches: the placement above counts every pair in every
+// segment (T^2 k / 64 counter updates in all).  Beyond kScanMinTokens the
+// counts go through a workspace instead: each segment's per-expert
+// histogram (route_count_kernel), then one workgroup turns them into each
+// segment's first position per expert and the expert offsets
+// (route_scan_kernel), and the placement starts from those.
+constexpr int kScanMinTokens = 4096;
+
+__global__ void __launch_bounds__(kSegThreads)
+route_count_kernel(const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ hist) {
+  __shared__ int s_cnt[kMaxE];
+  const int tid = threadIdx.x, seg = blockIdx.x;
+  const int p0 = seg * kSegTokens * k, p1 = std::min(T, (seg + 1) * kSegTokens) * k;
+  for (int e = tid; e < E; e += kSegThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int p = p0 + tid; p < p1; p += kSegThreads) atomicAdd(&s_cnt[ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kSegThreads) hist[(int64_t)seg * E + e] = s_cnt[e];
+}
+
+// One workgroup, one thread per expert: the exclusive prefix of its counts
+// over the segments (in batches of 16 segments, so a batch waits for memory
+// once), then the exclusive scan of the experts' totals (the offsets); each
+// segment's first position per expert is written over its histogram.
+__global__ void __launch_bounds__(kMaxE)
+route_scan_kernel(int nseg, int E, int32_t *__restrict__ hist, int32_t *__restrict__ offsets) {
+  __shared__ int s_tot[kMaxE];
+  __shared__ int s_off[kMaxE + 1];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int run = 0;
+  if (e < E) {
+    for (int s0 = 0; s0 < nseg; s0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = s0 + u < nseg ? hist[(int64_t)(s0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (s0 + u < nseg) hist[(int64_t)(s0 + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+  }
+  s_tot[e] = e < E ? run : 0;
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < E; base += kWave) {
+      const int x = base + lane;
+      const int cnt = x < E ? s_tot[x] : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+      }
+      if (x < E) s_off[x] = carry + incl - cnt;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) s_off[E] = carry;
+  }
+  __syncthreads();
+  if (e <= E) offsets[e] = s_off[e];
+  if (e == 0 && E == kMaxE) offsets[E] = s_off[E];
+  if (e < E) {
+    const int off = s_off[e];
+    for (int sg = 0; sg < nseg; ++sg) hist[(int64_t)sg * E + e] += off;
+  }
+}
 
 // Routing mass (PagedWeight review summary: routing-mass buckets protect
 // frequently used experts): m_e = sum of the gates of expert e's pairs.
@@ -177,11 +265,13 @@ using namespace moeq;
 
 // Up to kRouteSingleMax tokens: the single-workgroup kernel (one launch,
 // one wave per token); more: the top-k and placement kernels (measured:
-// 9.7 against 11.9 us at 64 tokens, 9.4 against 7.8 us at 16).  Neither
-// needs a workspace.
+// 9.7 against 11.9 us at 64 tokens, 9.4 against 7.8 us at 16).  The
+// workspace is needed only beyond kScanMinTokens tokens.
 constexpr int kRouteSingleMax = kRouteTokens;
 static inline bool route_single(int T) { return T <= kRouteSingleMax; }
-static inline size_t route_ws_bytes(int, int) { return 0; }
+static inline size_t route_ws_bytes(int T, int E) {
+  return T > kScanMinTokens ? (size_t)route_segments(T) * E * 4 : 0;
+}
 
 MOEQ_API moeq_status moeq_route_workspace_size(int32_t T, int32_t E, int32_t k, size_t *bytes) {
   if (!bytes) return fail(MOEQ_ERR_INVALID, "route_workspace_size: null output");
@@ -212,8 +302,14 @@ MOEQ_API moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32
   } else {
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkThreads), 0, stream,
                        logits, T, E, k, out->topk_ids, out->topk_gates);
+    int32_t *hist = nullptr;
+    if (need > 0) {
+      hist = static_cast<int32_t *>(ws);
+      hipLaunchKernelGGL(route_count_kernel, dim3(nseg), dim3(kSegThreads), 0, stream, out->topk_ids, T, E, k, hist);
+      hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kMaxE), 0, stream, nseg, E, hist, out->expert_offsets);
+    }
     hipLaunchKernelGGL(route_place_kernel, dim3(nseg), dim3(kSegThreads), 0, stream, out->topk_ids, T, E, k,
-                       out->expert_offsets, out->sorted_pairs, out->pair_pos);
+                       out->expert_offsets, out->sorted_pairs, out->pair_pos, (const int32_t *)hist);
   }
   prof_end("route", stream);
   return check_launch("route");

@@ -340,9 +340,11 @@ moeq_status moeq_route_workspace_size(int32_t T, int32_t E, int32_t k, size_t *b
  * sorted_pairs.  ([BEAM] top-k routing with top-n compensation; [MxMoE]
  * uneven expert activation.)
  *   logits DEVICE [T, E] fp32, finite.  T >= 0, 1 <= k <= E <= 256.
- *   ws DEVICE workspace of at least moeq_route_workspace_size bytes
- *   (may be NULL when that size is 0, which it is for every T in this
- *   version); a smaller one returns MOEQ_ERR_WORKSPACE.
+ *   ws DEVICE workspace of at least moeq_route_workspace_size bytes (may
+ *   be NULL when that size is 0, which it is up to T = 4096; beyond, it
+ *   holds per-64-token-segment expert histograms, ceil(T / 64) * E * 4
+ *   bytes, so that the sort's work stays linear in T); a smaller one
+ *   returns MOEQ_ERR_WORKSPACE.
  */
 moeq_status moeq_route(const float *logits, int32_t T, int32_t E, int32_t k,
                        const moeq_routing *out, void *ws, size_t ws_bytes,

@@ -61,11 +61,18 @@ def test_route_validation(L):
     assert L.moeq_route(ctypes.c_void_p(16), 4, 8, 9, ctypes.byref(r), None, 0, None) == 1
     assert L.moeq_route(ctypes.c_void_p(16), 4, 300, 2, ctypes.byref(r), None, 0, None) == 1
     assert L.moeq_route(ctypes.c_void_p(16), -1, 8, 2, ctypes.byref(r), None, 0, None) == 1
-    # neither the single-workgroup path (T <= 64) nor the two-kernel path
-    # (each placement segment counts all pairs itself) needs a workspace
-    for T, E, k in [(16, 8, 2), (64, 128, 8), (65, 128, 8), (4096, 8, 2), (1 << 20, 256, 8)]:
+    # up to 4096 tokens no workspace (each placement segment counts all
+    # pairs itself); beyond, one histogram of E counts per 64-token segment
+    for T, E, k in [(16, 8, 2), (64, 128, 8), (65, 128, 8), (4096, 8, 2)]:
         n = ctypes.c_size_t(7)
         assert L.moeq_route_workspace_size(T, E, k, ctypes.byref(n)) == 0 and n.value == 0
+    for T, E, k in [(4097, 8, 2), (8192, 256, 8), (1 << 20, 256, 8)]:
+        n = ctypes.c_size_t(7)
+        assert L.moeq_route_workspace_size(T, E, k, ctypes.byref(n)) == 0 and n.value == -(-T // 64) * E * 4
+    # a long batch without (or with too small) a workspace is rejected before
+    # anything is enqueued
+    assert L.moeq_route(ctypes.c_void_p(16), 4097, 8, 2, ctypes.byref(r), None, 0, None) == 3
+    assert L.moeq_route(ctypes.c_void_p(16), 4097, 8, 2, ctypes.byref(r), ctypes.c_void_p(16), 100, None) == 3
     n = ctypes.c_size_t(7)
     assert L.moeq_route_workspace_size(16, 8, 9, ctypes.byref(n)) == 1 and n.value == 7
 

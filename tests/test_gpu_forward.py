@@ -21,6 +21,8 @@ CASES = {
     "finegrained": ("finegrained", dict(T=16)),           # E 64 > 4 k: route, then FFN
     # fused, with shared factors (groups of 2) large in the output
     "tiny_shared": ("tiny", dict(T=16, rs=16, share=2, factor_std=0.05)),
+    # a long batch: the routing's workspace follows the FFN's in ws
+    "tiny_t4160": ("tiny", dict(T=4160)),
 }
 _cache = {}
 

@@ -52,6 +52,19 @@ def test_route_shapes_and_ties(T, E, k):
     _check(rng.standard_normal((T, E)).astype(np.float32), k)
 
 
+@pytest.mark.parametrize("T,E,k", [(4097, 8, 2), (8192, 256, 8), (5000, 64, 6)])
+def test_route_long_batches(T, E, k):
+    """Beyond 4096 tokens the sort counts through a workspace (per-segment
+    histograms, one scan over the segments): bit-exact against the oracle
+    on tied and untied logits, with a ragged last segment (4097, 5000)."""
+    from bit_quantized_moe_token_amd import moeq
+    rt = moeq.RoutingOut(T, E, k, "cuda")
+    assert rt.ws_bytes == -(-T // 64) * E * 4
+    rng = np.random.default_rng(T + E)
+    _check((rng.integers(-2, 3, size=(T, E)) * 0.25).astype(np.float32), k)
+    _check(rng.standard_normal((T, E)).astype(np.float32), k)
+
+
 def test_route_deterministic():
     cfg = configs.get("prefill")
     logits = gen.gen_logits(cfg, 0)
