@@ -60,10 +60,14 @@ def parse():
     p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
                    help="reduce a kernel trace and an SQ counter pass (MFMA, VALU) of the workload's command "
                         "to profiles/counters_<workload>.md")
-    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="no GPU work: reduce a rocprofv3 --kernel-trace --stats folder of the default "
+                        "bench command to profiles/kernels_<workload>.md")
+    p.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                    help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, "
-                        "WRITE_SIZE) of a --copy-calibration run and record the scaled "
-                        "per-launch HBM traffic of each kernel of the workload")
+                        "WRITE_SIZE) of a --copy-calibration run (and, optionally, the log of "
+                        "the FETCH run's bench line) and record the scaled per-launch HBM "
+                        "traffic of each kernel of the workload")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the extra measurements (prefill layer and the other three layers)")
     p.add_argument("--no-others", action="store_true",
@@ -435,6 +439,38 @@ def summarize_sq(workload, trace_dir, sq_dir):
     print("\n".join(lines))
 
 
+def summarize_trace(workload, trace_dir, top=30):
+    """Kernel-time table (calls, mean, min, max, share) of a rocprofv3
+    --kernel-trace --stats run of the default bench command (the workload,
+    the prefill layer and the other three layers, set-up included) to
+    profiles/kernels_<workload>.md."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(stats[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    short = workload_short(workload)
+    lines = [f"# Kernel time, {workload} (bench.py default command under rocprofv3)", "",
+             "Commands (from the repository root, on one MI355X):", "", "```",
+             f"cd /tmp && export TMPDIR=/tmp && cd - && rocprofv3 --kernel-trace --stats -d {trace_dir} -o kt "
+             f"--output-format csv -- python3 bench.py --no-cpu-baseline",
+             f"python3 bench.py --workload {short} --summarize-trace {trace_dir}", "```", "",
+             "Source `kt_kernel_stats.csv`: every kernel of the run (the decode layer, the prefill layer, the "
+             "tiny, fine-grained and bit-plane layers, and set-up: quantization, LUTs, packing), the "
+             f"{top} largest by total time. Durations in microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        name = r["Name"][:110]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"kernels_{short}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def workload_short(name):
     from synth import configs
     for short in ("decode", "prefill", "finegrained", "bitplane", "tiny"):
@@ -443,7 +479,13 @@ def workload_short(name):
     return name
 
 
-def summarize_pmc(workload, fetch_dir, write_dir):
+def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
+    """Per-launch HBM traffic (FETCH_SIZE, WRITE_SIZE passes, each scaled by
+    what it reads for the calibration copy) of each kernel of the workload:
+    stored in profiles/traffic_counters.json (with the kernel source hash)
+    and written out as profiles/traffic_<workload>.md, beside the
+    algorithmic bytes of the layer and of its gate/up launch when the
+    profiled run's bench line (bench_log) is given."""
     fe = _read_pmc(fetch_dir, "FETCH_SIZE")
     wr = _read_pmc(write_dir, "WRITE_SIZE")
     # each counter is scaled by what it reads for the copy of CALIB_BYTES
@@ -460,6 +502,40 @@ def summarize_pmc(workload, fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(tr, fh, indent=1, sort_keys=True)
     print(json.dumps({workload: ent}, indent=1))
+    short = workload_short(workload)
+    rx = "gateup_kernel|down_kernel|lowrank|route|combine|neg_kernel"
+    cmd = (f"python3 bench.py --workload {short} --steps 20 --warmup 5 --no-cpu-baseline --no-extra "
+           f"--copy-calibration")
+    lines = [f"# HBM traffic per launch, {workload}", "",
+             "Two counter passes (one counter each) and their reduction to bytes per launch:", "", "```",
+             f'rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "{rx}" -d {fetch_dir} -o pmc '
+             f"--output-format csv -- {cmd}",
+             f'rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "{rx}" -d {write_dir} -o pmc '
+             f"--output-format csv -- {cmd}",
+             f"python3 bench.py --workload {short} --summarize-pmc {fetch_dir} {write_dir}"
+             + (f" {bench_log}" if bench_log else ""), "```", "",
+             f"The calibration kernel is an int8 negation over 1 GiB (reads and writes 2^30 B once each). "
+             f"Scale factors (bytes per counted byte): FETCH_SIZE x{cf:.4f}, WRITE_SIZE x{cw:.4f}. "
+             f"Kernel sources hash `{ent['source_hash']}`.", "",
+             "| kernel | launches | fetch MB | write MB | total MB |", "|---|---|---|---|---|"]
+    for key, v in sorted(ent["kernels"].items()):
+        lines.append(f"| {key} | {v['launches']} | {v['fetch_bytes'] / 1e6:.3f} | {v['write_bytes'] / 1e6:.3f} | "
+                     f"{v['bytes'] / 1e6:.3f} |")
+    if bench_log and os.path.exists(bench_log):
+        line = [l for l in open(bench_log) if l.startswith("{")][-1]
+        b = json.loads(line)
+        lay = b.get("layer", {})
+        lines += ["", f"Algorithmic bytes of the profiled call (the bench line of the FETCH pass): the layer "
+                      f"{lay.get('alg_bytes', 0) / 1e6:.3f} MB; its gate/up launch (codes, metadata and U of "
+                      f"the gate and up blocks of the active experts, x read, h written) "
+                      f"{b['roofline']['bytes_per_launch'] / 1e6:.3f} MB."]
+        gu = ent["kernels"].get("gateup_stream")
+        if gu:
+            lines.append(f"Counter traffic of the gate/up launch over its algorithmic bytes: "
+                         f"{gu['bytes'] / b['roofline']['bytes_per_launch']:.3f}.")
+    lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"traffic_{short}.md"), "w") as fh:
+        fh.write("\n".join(lines))
 
 
 def cpu_baseline(cfg, seed, sample_tokens, min_seconds=12.0):
@@ -517,6 +593,10 @@ def main():
     if args.summarize_pmc:
         from synth import configs
         summarize_pmc(configs.get(args.workload)["name"], *args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        from synth import configs
+        summarize_trace(configs.get(args.workload)["name"], args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the expert layer is not "
