@@ -281,7 +281,10 @@ def copy_calibration():
 
 
 # rocprofv3 kernel names -> the names the library's own profiler uses
-KERNEL_KEYS = [("gateup_kernel", "gateup_stream"), ("down_kernel", "down_stream"),
+# kernel name pattern -> key; the tiled kernels' names contain the streaming
+# kernels' names, so they are matched first
+KERNEL_KEYS = [("tiled_gateup", "gateup_tiled"), ("tiled_down", "down_tiled"),
+               ("gateup_kernel", "gateup_stream"), ("down_kernel", "down_stream"),
                ("route", "route"), ("combine", "combine"), ("neg_kernel", "calibration_copy")]
 
 
@@ -529,7 +532,7 @@ def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
                       f"{lay.get('alg_bytes', 0) / 1e6:.3f} MB; its gate/up launch (codes, metadata and U of "
                       f"the gate and up blocks of the active experts, x read, h written) "
                       f"{b['roofline']['bytes_per_launch'] / 1e6:.3f} MB."]
-        gu = ent["kernels"].get("gateup_stream")
+        gu = ent["kernels"].get("gateup_stream") or ent["kernels"].get("gateup_tiled")
         if gu:
             lines.append(f"Counter traffic of the gate/up launch over its algorithmic bytes: "
                          f"{gu['bytes'] / b['roofline']['bytes_per_launch']:.3f}.")

@@ -245,6 +245,52 @@ def test_mixed_bits_shared_factors_brute_force(fmt):
         assert np.allclose(y, _brute_dense(layer, x, logits, k, n_comp), rtol=1e-12, atol=1e-12)
 
 
+def test_shared_down_term_once_per_token_group():
+    """The down side of shared factors applied once per (token, expert
+    group) to the gate-weighted sum, sum_e g_e U_G (V_G h_e) =
+    U_G (sum_e g_e V_G h_e), gives the routed layer of the per-pair
+    definition; the gate/up side's V_G x is the same for every member of a
+    (token, group).  Explicit loops over the groups; 8 experts in groups of
+    4, top-4, so tokens hit several experts of a group; every n_comp."""
+    rng = np.random.default_rng(21)
+    E, H, I, G, T, k, share = 8, 16, 24, 8, 10, 4, 4
+    layer = _random_layer(rng, E, H, I, G, 3, r=2, rs=3, share=share)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    rt = forward.route(logits, k)
+    for n_comp in (1, 2, 4):
+        y = forward.moe_forward(layer, x, logits, k, n_comp)
+        y2 = np.zeros((T, H))
+        for t in range(T):
+            xt = x[t:t + 1].astype(np.float64)
+            wsum = {}                 # group -> sum_j g_j V_G h_j over compensated slots
+            for j in range(k):
+                e, g = int(rt["ids"][t, j]), float(rt["gates"][t, j])
+                comp = np.array([j < n_comp])
+                grp = layer.group_of(e)
+                a = forward.compensated_linear(forward.dequant_block(layer.qblock(e, 0), G), xt, comp,
+                                               layer.factors(e, 0), layer.shared(grp, 0))
+                b = forward.compensated_linear(forward.dequant_block(layer.qblock(e, 1), G), xt, comp,
+                                               layer.factors(e, 1), layer.shared(grp, 1))
+                h = forward.silu(a) * b
+                # dense and per-expert terms per pair; the shared term deferred
+                yp = forward.compensated_linear(forward.dequant_block(layer.qblock(e, 2), G), h, comp,
+                                                layer.factors(e, 2), None)
+                y2[t] += g * yp[0]
+                if j < n_comp:
+                    Ug, Vg = (f.astype(np.float64) for f in layer.shared(grp, 2))
+                    wsum[grp] = wsum.get(grp, 0.0) + g * (Vg @ h[0])
+            for grp, w in wsum.items():
+                Ug = layer.shared(grp, 2)[0].astype(np.float64)
+                y2[t] += Ug @ w
+        assert np.allclose(y2, y, rtol=1e-12, atol=1e-12)
+        # some token routes two compensated slots to one group (the case
+        # the deduplication changes)
+        if n_comp >= 2:
+            gi = rt["ids"][:, :n_comp] // share
+            assert any(len(set(row)) < n_comp for row in gi.tolist())
+
+
 def test_compensated_linear_equals_dense_sum():
     """W_hat v + U(V v) + U_G(V_G v) == (W_hat + U V + U_G V_G) v, and rank 0
     (no factors, or comp off) is the plain quantized layer."""
