@@ -57,9 +57,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
-    p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
+    p.add_argument("--summarize-sq", nargs="+", metavar="DIR",
                    help="reduce a kernel trace and an SQ counter pass (MFMA, VALU) of the workload's command "
-                        "to profiles/counters_<workload>.md")
+                        "(and, optionally, a pass of the stall and LDS counters) to "
+                        "profiles/counters_<workload>.md")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: reduce a rocprofv3 --kernel-trace --stats folder of the default "
                         "bench command to profiles/kernels_<workload>.md")
@@ -368,6 +369,9 @@ SQ_KEYS = [("tiled_gateup", "gateup_tiled"), ("tiled_down", "down_tiled"), ("gat
            ("down_kernel", "down_stream"), ("lowrank", "lowrank_project"), ("route", "route"), ("combine", "combine")]
 SQ_COUNTERS = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_WAVES", "SQ_BUSY_CYCLES",
                "GRBM_GUI_ACTIVE"]
+# the optional second pass: where the waves' cycles go, and the LDS
+SQ_STALL_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY",
+                     "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"]
 MFMA_FLOPS = 16 * 16 * 32 * 2      # every MFMA of these kernels is v_mfma_f32_16x16x32_f16
 N_SIMD = 256 * 4
 N_XCD = 8                           # GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs
@@ -377,7 +381,25 @@ def _sq_key(name):
     return next((k for pat, k in SQ_KEYS if pat in name), None)
 
 
-def summarize_sq(workload, trace_dir, sq_dir):
+def _read_sq(folder, names):
+    """Per kernel key, per counter: the per-dispatch values under folder."""
+    import csv
+    import glob
+    per = {}
+    for fn in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(fn)):
+            key = _sq_key(row.get("Kernel_Name", ""))
+            if key is None or row.get("Counter_Name") not in names:
+                continue
+            d = (fn, row["Dispatch_Id"], key, row["Counter_Name"])
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+    vals = {}
+    for (_, _, key, cn), v in per.items():
+        vals.setdefault(key, {}).setdefault(cn, []).append(v)
+    return vals
+
+
+def summarize_sq(workload, trace_dir, sq_dir, stall_dir=None):
     """MFMA and VALU counters per kernel from one rocprofv3 --pmc pass
     (SQ_COUNTERS) and the kernel trace of the same command: MFMA
     instructions x 16384 flops over the mean duration (counter TFLOP/s), the
@@ -394,17 +416,7 @@ def summarize_sq(workload, trace_dir, sq_dir):
         if key:
             c, t = dur.get(key, (0, 0.0))
             dur[key] = (c + int(row["Calls"]), t + float(row["TotalDurationNs"]))
-    per = {}
-    for fn in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
-        for row in csv.DictReader(open(fn)):
-            key = _sq_key(row.get("Kernel_Name", ""))
-            if key is None or row.get("Counter_Name") not in SQ_COUNTERS:
-                continue
-            d = (fn, row["Dispatch_Id"], key, row["Counter_Name"])
-            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
-    vals = {}
-    for (_, _, key, cn), v in per.items():
-        vals.setdefault(key, {}).setdefault(cn, []).append(v)
+    vals = _read_sq(sq_dir, SQ_COUNTERS)
     lines = [f"# MFMA and VALU counters per kernel, {workload}", "",
              "Two runs of the same command (a kernel trace, then one counter pass with "
              f"{' '.join(SQ_COUNTERS)}) and their reduction:", "", "```",
@@ -435,6 +447,30 @@ def summarize_sq(workload, trace_dir, sq_dir):
         lines.append(f"| {key} | {len(vals[key].get('SQ_INSTS_MFMA', []))} | {us:.1f} | {mf:.4g} | {tf:.1f} | "
                      f"{tf / MFMA_F16_PEAK_TFLOPS:.3f} | {busy:.3f} | {v.get('SQ_INSTS_VALU', 0.0):.4g} | "
                      f"{v.get('SQ_WAVES', 0.0):.4g} | {clk:.2f} |")
+    if stall_dir:
+        sv = _read_sq(stall_dir, SQ_STALL_COUNTERS)
+        lines += ["", "Where the waves' cycles go, from a second counter pass of the same command:", "", "```",
+                  f"rocprofv3 --pmc {' '.join(SQ_STALL_COUNTERS)} -d {stall_dir} -o pmc --output-format csv -- "
+                  f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline "
+                  f"--no-extra", "```", "",
+                  "Shares of SQ_WAVE_CYCLES (the summed lifetime of the kernel's waves): issuing any instruction, "
+                  "issuing VALU instructions (MFMAs included), waiting at a wait or barrier (SQ_WAIT_ANY), and "
+                  "ready but not issued (SQ_WAIT_INST_ANY: a dependency or a busy unit). LDS: instructions per "
+                  "dispatch, and the LDS bank-conflict cycles over the LDS-active cycles.", "",
+                  "| kernel | issue any | issue VALU | waiting | not issued | LDS instr | bank-conflict share |",
+                  "|---|---|---|---|---|---|---|"]
+        for key in [k for _, k in SQ_KEYS]:
+            if key not in sv:
+                continue
+            v = {cn: stat(x) for cn, x in sv[key].items()}
+            wc = v.get("SQ_WAVE_CYCLES", 0.0)
+            lds = v.get("SQ_ACTIVE_INST_LDS", 0.0)
+            if not wc:
+                continue
+            lines.append(f"| {key} | {v.get('SQ_ACTIVE_INST_ANY', 0.0) / wc:.3f} | "
+                         f"{v.get('SQ_ACTIVE_INST_VALU', 0.0) / wc:.3f} | {v.get('SQ_WAIT_ANY', 0.0) / wc:.3f} | "
+                         f"{v.get('SQ_WAIT_INST_ANY', 0.0) / wc:.3f} | {v.get('SQ_INSTS_LDS', 0.0):.4g} | "
+                         f"{(v.get('SQ_LDS_BANK_CONFLICT', 0.0) / lds) if lds else 0.0:.3f} |")
     lines.append("")
     out = os.path.join(ROOT, "profiles", f"counters_{workload_short(workload)}.md")
     with open(out, "w") as fh:

@@ -26,13 +26,22 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  The tiled kernels keep their MFMA accumulators in
+# ordinary VGPRs: with the accumulation-register form the allocator
+# permutes the loop-carried accumulators through copies on every K tile.
+FILE_FLAGS = {
+    "tiled_gu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "tiled_dn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

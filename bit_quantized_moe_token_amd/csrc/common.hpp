@@ -114,6 +114,14 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same with every LDS read (and scalar load) of this wave completed too
+// (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void lgkm_vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 // Buffer resource over [base, base + bytes) for the raw buffer loads below
 // (dword 3: the gfx9 default data format; offsets past `bytes` read zero).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {

@@ -7,12 +7,15 @@
 //   - a workgroup computes a 128-token x 256-row output tile of one expert
 //     (gate/up: 128 rows of I for both gate and up, so SwiGLU is formed in
 //     registers; down: 256 rows of H);
-//   - 4 waves, each owning 4 strips of 16 rows over all 128 tokens: 32
-//     MFMA 16x16x32 tiles per 32-column step;
+//   - 8 waves (two per SIMD, so that one wave's MFMAs run while the other
+//     decodes or waits), each owning 2 strips of 16 rows over all 128
+//     tokens: 16 MFMA 16x16x32 tiles per 32-column step;
 //   - K walks 128-column tiles through three LDS stages filled by LDS-DMA
-//     loads two tiles ahead (activation rows gathered by token for gate/up,
-//     XOR-swizzled; the packed codes, whose layout already is the MFMA
-//     B-operand layout per lane), one barrier per tile;
+//     loads issued three tiles ahead (activation rows gathered by token
+//     for gate/up, XOR-swizzled; the packed codes, whose layout already is
+//     the MFMA B-operand layout per lane), one barrier per tile; within a
+//     tile the next 32-column step's activation reads and weight decode
+//     are spread between the current step's MFMAs;
 //   - INT codes decode to fp16 s*(c - z): exact (c - z) from the magic-bias
 //     AND-OR and one packed FMA, then one packed multiply by the group's
 //     fp16 scale (rounded once to fp16);
@@ -25,7 +28,7 @@ namespace moeq {
 
 constexpr int kTM = kTiledM;           // tokens per token tile
 constexpr int kH32S = kTileK + 4;      // LDS row stride (floats) of the staged fp32 h tile
-constexpr int kTiledWaves = 4;   // waves per workgroup (8 token tiles x 4 strips each)
+constexpr int kTiledWaves = 8;   // waves per workgroup (8 token tiles x 2 strips each)
 
 // Packed codes and metadata of one strip for one 128-column tile.
 template <int B>
@@ -75,17 +78,18 @@ __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
 // ---- LDS stages.  A stage holds one 128-column tile: the activation tile
 // (128 token rows x 256 B, 16-byte slots XOR-swizzled by row so that the
 // MFMA operand reads are bank-conflict free), the packed codes of the
-// workgroup's 16 strips (1 KiB each) and their scales and zeros.  All of
-// it is written by the LDS forms of the loads (activations and codes:
-// buffer_load ... lds against buffer resources, i.e. a scalar base plus a
-// 32-bit lane offset; scales and zeros: global_load_lds): the data never
-// occupies registers, so tiles are fetched two ahead of the
-// MFMAs through three stages, and the only memory counter the loop waits
-// on is the one for these transfers (explicit waits: the compiler does not
-// track DMA writes into LDS).
+// workgroup's 16 strips (1 KiB each) and their scales and zeros (a
+// 512-byte slot per wave).  All of it is written by the LDS forms of the
+// loads (activations and codes: buffer_load ... lds against buffer
+// resources, i.e. a scalar base plus a 32-bit lane offset; scales and
+// zeros: global_load_lds): the data never occupies registers, and the only
+// memory counter the loop waits on is the one for these transfers
+// (explicit waits: the compiler does not track DMA writes into LDS).
+// Staging the same loads through registers (buffer loads, then LDS
+// stores) measured slower.
 constexpr int kTABytes = kTM * 256;
 constexpr int kTBBytes = 16 * 1024;
-constexpr int kTMetaBytes = 4 * 512;                  // per wave: 64 lanes x 2 dword slots
+constexpr int kTMetaBytes = kTiledWaves * 512;        // per wave: 64 lanes x 2 dword slots
 constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
 constexpr int kTStages = 3;
 constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
@@ -130,12 +134,13 @@ __device__ __forceinline__ f16x8 tlds_a(const uint8_t *abuf, int s, int j) {
   return *reinterpret_cast<const f16x8 *>(abuf + row * 256 + 16 * (c ^ (row & 15)));
 }
 
-// The strips of wave w: q = 0, 1 from block d0 (bits B0), q = 2, 3 from d1
-// (bits B1); their codes sit at 1 KiB slots 4 w + q of the stage, their
-// scales/zeros in lanes 16 q .. 16 q + 15 of the wave's metadata slots.
+// The strips of wave w: q = 0 from block d0 (bits B0), q = 1 from d1 (bits
+// B1); their codes sit at 1 KiB slots 2 w + q of the stage, their scales
+// and zeros in lanes 16 q .. 16 q + 15 of the wave's metadata slots (lanes
+// 32 .. 63 repeat lanes 0 .. 31).
 template <int B0, int B1, int GPT>
 struct TKLoop {
-  static constexpr int kDma = 8 + 2 * dma_ops(B0) + 2 * dma_ops(B1) + 2;   // DMA ops per tile per wave
+  static constexpr int kDma = 4 + dma_ops(B0) + dma_ops(B1) + 2;   // DMA ops per tile per wave
   const BlockDesc &d0, &d1;
   const int *strips;
   int n_kt, wave;
@@ -143,99 +148,125 @@ struct TKLoop {
   uint8_t *lds;
   __amdgpu_buffer_rsrc_t ra, rc0, rc1;   // activations, codes of d0 and of d1
 
-  __device__ __forceinline__ uint8_t *stage(int st) const { return lds + st * kTStageBytes; }
-
-  // tile t into stage st: the wave's 8 KiB share of the activation tile,
-  // its strips' codes, scales and zeros
-  __device__ __forceinline__ void issue(int t, int st) const {
+  // tile t into the stage at byte offset sb: the wave's 4 KiB share of the
+  // activation tile (rows 16 w .. 16 w + 15), its strips' codes, scales and
+  // zeros
+  __device__ __forceinline__ void issue(int t, uint32_t sb) const {
     const int lane = threadIdx.x & 63;
-    uint8_t *a = stage(st);
+    uint8_t *a = lds + sb;
     // buffer loads: uniform tile offset + loop-invariant 32-bit lane offset
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 32 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
       const uint32_t c = (uint32_t)((lane & 15) ^ (row & 15));
-      lds_dma_buf<16>(ra, 2u * (rowoff[i] + 8u * c), (uint32_t)t * (kTileK * 2), a + (32 * wave + 4 * i) * 256);
+      lds_dma_buf<16>(ra, 2u * (rowoff[i] + 8u * c), (uint32_t)t * (kTileK * 2), a + (16 * wave + 4 * i) * 256);
     }
-    uint8_t *b = stage(st) + kTABytes + 4 * wave * 1024;
+    uint8_t *b = a + kTABytes + 2 * wave * 1024;
     dma_codes<B0>(rc0, strips[0], t, n_kt, b);
-    dma_codes<B0>(rc0, strips[1], t, n_kt, b + 1024);
-    dma_codes<B1>(rc1, strips[2], t, n_kt, b + 2048);
-    dma_codes<B1>(rc1, strips[3], t, n_kt, b + 3072);
-    // lane l: strip q = l / 16, row l % 16
-    const int q = lane >> 4;
-    const BlockDesc &dq = q < 2 ? d0 : d1;
-    const uint64_t mi = meta_index(strips[q], t, lane & 15, 0, n_kt, GPT);
-    uint8_t *m = stage(st) + kTABytes + kTBBytes + wave * 512;
+    dma_codes<B1>(rc1, strips[1], t, n_kt, b + 1024);
+    // lane l: strip q = (l / 16) % 2, row l % 16
+    const int q = (lane >> 4) & 1;
+    const BlockDesc &dq = q == 0 ? d0 : d1;
+    const uint64_t mi = meta_index(q == 0 ? strips[0] : strips[1], t, lane & 15, 0, n_kt, GPT);
+    uint8_t *m = a + kTABytes + kTBBytes + wave * 512;
     lds_dma<2 * GPT>(dq.scales + mi, m);       // dword slot per lane
     lds_dma<GPT>(dq.zeros + mi, m + 256);      // zero-extended dword slot per lane
   }
 
-  template <int NT>
-  __device__ __forceinline__ void compute(int st, f32x4 (*acc)[NT]) const {
-    const int lane = threadIdx.x & 63;
-    const uint8_t *a = stage(st);
-    const uint8_t *b = stage(st) + kTABytes + 4 * wave * 1024;
-    const uint8_t *m = stage(st) + kTABytes + kTBBytes + wave * 512;
-    TTile<B0> t0, t1;
-    TTile<B1> t2, t3;
+  // the codes, scales and zeros of the wave's strips from the stage at sb
+  __device__ __forceinline__ void load_codes(uint32_t sb, TTile<B0> &t0, TTile<B1> &t1) const {
+    const int r = threadIdx.x & 15;
+    const uint8_t *b = lds + sb + kTABytes + 2 * wave * 1024;
+    const uint8_t *m = lds + sb + kTABytes + kTBBytes + wave * 512;
     lds_codes<B0>(b, t0);
-    lds_codes<B0>(b + 1024, t1);
-    lds_codes<B1>(b + 2048, t2);
-    lds_codes<B1>(b + 3072, t3);
-    const int r = lane & 15;
+    lds_codes<B1>(b + 1024, t1);
     const uint32_t *sc = reinterpret_cast<const uint32_t *>(m);
     const uint32_t *zz = reinterpret_cast<const uint32_t *>(m + 256);
-    t0.sc = sc[r]; t1.sc = sc[16 + r]; t2.sc = sc[32 + r]; t3.sc = sc[48 + r];
-    t0.zz = zz[r]; t1.zz = zz[16 + r]; t2.zz = zz[32 + r]; t3.zz = zz[48 + r];
-    // activation fragments double-buffered across steps: step j + 1's NT
-    // reads are in flight while step j is decoded and multiplied
-    f16x8 av[2][NT];
+    t0.sc = sc[r]; t1.sc = sc[16 + r];
+    t0.zz = zz[r]; t1.zz = zz[16 + r];
+  }
+
+  // activation fragments of step j of the tile in the stage at sb
+  template <int NT>
+  __device__ __forceinline__ void load_a(uint32_t sb, int j, f16x8 *av) const {
 #pragma unroll
-    for (int s = 0; s < NT; ++s) av[0][s] = tlds_a(a, s, 0);
+    for (int s = 0; s < NT; ++s) av[s] = tlds_a(lds + sb, s, j);
+  }
+
+  __device__ __forceinline__ static void decode(const TTile<B0> &t0, const TTile<B1> &t1, int j, f16x8 *w) {
+    w[0] = tdecode<B0, GPT>(t0, j);
+    w[1] = tdecode<B1, GPT>(t1, j);
+  }
+
+  // the two MFMAs of token sub-tile s of a step
+  template <int NT>
+  __device__ __forceinline__ static void mma_s(f16x8 av, const f16x8 *w, f32x4 (*acc)[NT], int s) {
+    acc[0][s] = mfma16(av, w[0], acc[0][s]);
+    acc[1][s] = mfma16(av, w[1], acc[1][s]);
+  }
+
+  // One 32-column step: the MFMAs of the step (weights wc, activation
+  // fragments av), each fragment replaced by the next step's (step jn of
+  // the stage at sn) once its MFMAs are issued, and the next step's
+  // weights decoded into wn between them.
+  template <int NT>
+  __device__ __forceinline__ void step(f16x8 *av, const f16x8 *wc, f16x8 *wn, f32x4 (*acc)[NT], uint32_t sn,
+                                       int jn, const TTile<B0> &t0, const TTile<B1> &t1) const {
+    decode(t0, t1, jn, wn);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < 3) {
-#pragma unroll
-        for (int s = 0; s < NT; ++s) av[(j + 1) & 1][s] = tlds_a(a, s, j + 1);
-      }
-      const f16x8 w0 = tdecode<B0, GPT>(t0, j), w1 = tdecode<B0, GPT>(t1, j);
-      const f16x8 w2 = tdecode<B1, GPT>(t2, j), w3 = tdecode<B1, GPT>(t3, j);
-#pragma unroll
-      for (int s = 0; s < NT; ++s) {
-        acc[0][s] = mfma16(av[j & 1][s], w0, acc[0][s]);
-        acc[1][s] = mfma16(av[j & 1][s], w1, acc[1][s]);
-        acc[2][s] = mfma16(av[j & 1][s], w2, acc[2][s]);
-        acc[3][s] = mfma16(av[j & 1][s], w3, acc[3][s]);
-      }
+    for (int s = 0; s < NT; ++s) {
+      mma_s<NT>(av[s], wc, acc, s);
+      av[s] = tlds_a(lds + sn, s, jn);
     }
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // one K tile: wait for its stage (the next tile's transfers may stay in
-  // flight), barrier (every wave's transfers done; every wave has finished
-  // reading the stage of tile t - 1), queue tile t + 2 into that stage,
-  // multiply
-  template <int ST, int NT>
-  __device__ __forceinline__ void step(int t, f32x4 (*acc)[NT]) const {
-    vm_wait<kDma>();
-    __builtin_amdgcn_s_barrier();
-    issue(std::min(t + 2, n_kt - 1), (ST + 2) % 3);
-    compute<NT>(ST, acc);
-  }
-
+  // The K walk as a software pipeline over 32-column steps: while the
+  // MFMAs of step j run, the activation fragments of step j + 1 are read
+  // and its weights decoded.  Tile t + 1's stage is opened (wait for its
+  // transfers, barrier) before the last step of tile t, whose weights are
+  // already decoded, so that step reads tile t + 1's codes and first
+  // activation fragments and decodes its first step.  Transfers run three
+  // tiles ahead; tile t + 3 goes into tile t's stage once every wave has
+  // passed that barrier with all its reads of the stage completed.
   template <int NT>
   __device__ __forceinline__ void run(f32x4 (*acc)[NT]) const {
     issue(0, 0);
-    issue(std::min(1, n_kt - 1), 1);
-    int kt = 0;
+    issue(std::min(1, n_kt - 1), kTStageBytes);
+    issue(std::min(2, n_kt - 1), 2 * kTStageBytes);
+    vm_wait<2 * kDma>();
+    __builtin_amdgcn_s_barrier();
+    TTile<B0> t0;
+    TTile<B1> t1;
+    f16x8 av[NT], w0[2], w1[2];
+    load_codes(0, t0, t1);
+    load_a<NT>(0, 0, av);
+    decode(t0, t1, 0, w0);
+    uint32_t sb = 0;     // stage of tile t
 #pragma unroll 1
-    for (; kt + 3 <= n_kt; kt += 3) {
-      step<0, NT>(kt, acc);
-      step<1, NT>(kt + 1, acc);
-      step<2, NT>(kt + 2, acc);
+    for (int t = 0; t < n_kt; ++t) {
+      step<NT>(av, w0, w1, acc, sb, 1, t0, t1);
+      step<NT>(av, w1, w0, acc, sb, 2, t0, t1);
+      step<NT>(av, w0, w1, acc, sb, 3, t0, t1);
+      // open tile t + 1 (on the last tile: a stage of re-read data whose
+      // values go unused)
+      lgkm_vm_wait<kDma>();
+      __builtin_amdgcn_s_barrier();
+      const uint32_t sn = sb == 2 * kTStageBytes ? 0u : sb + kTStageBytes;
+      issue(std::min(t + 3, n_kt - 1), sb);
+      load_codes(sn, t0, t1);
+      __builtin_amdgcn_sched_barrier(0);
+      step<NT>(av, w1, w0, acc, sn, 0, t0, t1);
+      sb = sn;
     }
-    if (kt < n_kt) step<0, NT>(kt, acc);
-    if (kt + 1 < n_kt) step<1, NT>(kt + 1, acc);
     // the queued re-reads of the last tile land before the LDS is reused
     vm_wait<0>();
     __syncthreads();
@@ -247,28 +278,28 @@ struct TKLoop {
 // XCD a contiguous run of tiles.
 __device__ __forceinline__ int xcd_tile(int b, int n) { return (b & 7) * (n >> 3) + (b >> 3); }
 
-// gate/up: wave w owns I rows nt*128 + 32 w + [0, 32) of gate (q = 0, 1)
-// and up (q = 2, 3), for all 128 tokens of the tile.
+// gate/up: wave w owns I rows nt*128 + 16 w + [0, 16) of gate (q = 0) and
+// up (q = 1), for all 128 tokens of the tile.
 template <int BG, int BU, int GPT>
 __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BlockDesc dg = a.desc[3 * ch.e], du = a.desc[3 * ch.e + 1];
-  const int sg = nt * 8 + 2 * wave;
-  const int strips[4] = {sg, sg + 1, sg, sg + 1};
-  uint32_t rowoff[8];          // activation rows this lane moves: 32 w + 4 i + lane / 16
+  const int sg = nt * 8 + wave;
+  const int strips[2] = {sg, sg};
+  uint32_t rowoff[4];          // activation rows this lane moves: 16 w + 4 i + lane / 16
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
+  for (int i = 0; i < 4; ++i) {
+    const int m = std::min(16 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
     rowoff[i] = (uint32_t)(a.sorted_pairs[ch.base + m] / a.k) * (uint32_t)a.H;
   }
   // the rows' x exponents: requested now, stored past the LDS stages after
   // the K walk (so that nothing waits for them)
   const int preg = threadIdx.x < kTM ? a.sorted_pairs[ch.base + std::min((int)threadIdx.x, ch.cnt - 1)] : 0;
   const int kreg = threadIdx.x < kTM ? a.xexp[preg / a.k] : 0;
-  f32x4 acc[4][8];
+  f32x4 acc[2][8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const TKLoop<BG, BU, GPT> kl{dg,
@@ -286,12 +317,12 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   // the epilogue does not wait for memory
   const int zw = 2 * a.RZ;
   const bool zpre = a.comp_on && a.ks_gu == 1 && zw <= 64 && a.rs == 0;
-  ZPre<8, 4, 8> zp;
-  if (zpre) z_preload<8, 4, 8>(a.zp_gu, zw, zw, ch, zp);
-  f16x8 ub[4];
+  ZPre<8, kTiledWaves, 4> zp;
+  if (zpre) z_preload<8, kTiledWaves, 4>(a.zp_gu, zw, zw, ch, zp);
+  f16x8 ub[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    ub[q] = a.comp_on && a.r > 0 ? lowrank_bop((q >> 1) ? du.U : dg.U, a.r, strips[q] * 16 + (lane & 15), 0)
+  for (int q = 0; q < 2; ++q)
+    ub[q] = a.comp_on && a.r > 0 ? lowrank_bop(q ? du.U : dg.U, a.r, strips[q] * 16 + (lane & 15), 0)
                                  : pack_b(0, 0, 0, 0);
   kl.template run<8>(acc);
   // acc holds W x~ (x~ = x 2^K, the normalised rows), as do the z rows
@@ -305,16 +336,15 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
   if (a.comp_on) {
     uint16_t *zs = l16;
-    if (zpre) z_store<8, 4, 8>(a, ch, s_kx, zp, zw, zs);
-    else z_prologue<8, 4>(a, true, a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
+    if (zpre) z_store<8, kTiledWaves, 4>(a, ch, s_kx, zp, zw, zs);
+    else z_prologue<8, kTiledWaves>(a, true, a.zp_gu, zw, a.ks_stride_gu, a.ks_gu, zw, ch, zs);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int b = q >> 1;
-      const BlockDesc &d = b ? du : dg;
+    for (int q = 0; q < 2; ++q) {
+      const BlockDesc &d = q ? du : dg;
       const int row = strips[q] * 16 + (lane & 15);
-      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs + b * a.RZ, zw, acc[q], ub[q]);
-      if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + b * a.RZ + a.Rp, zw, acc[q]);
+      if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs + q * a.RZ, zw, acc[q], ub[q]);
+      if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + q * a.RZ + a.Rp, zw, acc[q]);
     }
     __syncthreads();
   }
@@ -327,11 +357,8 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * s + 4 * (lane >> 4) + i;
       const int K = -s_kx[m];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const float gv = __builtin_ldexpf(acc[g][s][i], K), uv = __builtin_ldexpf(acc[2 + g][s][i], K);
-        h32[m * kH32S + 32 * wave + 16 * g + (lane & 15)] = gv / (1.0f + __expf(-gv)) * uv;
-      }
+      const float gv = __builtin_ldexpf(acc[0][s][i], K), uv = __builtin_ldexpf(acc[1][s][i], K);
+      h32[m * kH32S + 16 * wave + (lane & 15)] = gv / (1.0f + __expf(-gv)) * uv;
     }
   }
   __syncthreads();
@@ -339,9 +366,10 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   // |h| gives eb, then h 2^(kNormTop - eb) as fp16; eb goes to hblk for both
   // 64-column halves of this 128-column block
   const int tid = threadIdx.x, c8 = 8 * (tid & 15);
+  constexpr int kRowsPerPass = kTiledWaves * 64 / 16;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 4) + 16 * i;
+  for (int i = 0; i < kTM / kRowsPerPass; ++i) {
+    const int r = (tid >> 4) + kRowsPerPass * i;
     const f32x4 v0 = *reinterpret_cast<const f32x4 *>(h32 + r * kH32S + c8);
     const f32x4 v1 = *reinterpret_cast<const f32x4 *>(h32 + r * kH32S + c8 + 4);
     float mx = 0.f;
@@ -362,23 +390,23 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   }
 }
 
-// down: wave w owns H rows nt*256 + 64 w + [0, 64).
+// down: wave w owns H rows nt*256 + 32 w + [0, 32).
 template <int BD, int GPT>
 __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BlockDesc d = a.desc[3 * ch.e + 2];
-  const int s0 = nt * 16 + 4 * wave;
-  const int strips[4] = {s0, s0 + 1, s0 + 2, s0 + 3};
-  uint32_t rowoff[8];
+  const int s0 = nt * 16 + 2 * wave;
+  const int strips[2] = {s0, s0 + 1};
+  uint32_t rowoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = std::min(32 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
+  for (int i = 0; i < 4; ++i) {
+    const int m = std::min(16 * wave + 4 * i + (lane >> 4), ch.cnt - 1);
     rowoff[i] = (uint32_t)(ch.base + m) * (uint32_t)a.I;       // rows of the normalised h
   }
-  f32x4 acc[4][8];
+  f32x4 acc[2][8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.codes, code_region_bytes(d));
@@ -387,10 +415,10 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   kl.template run<8>(acc);
   if (a.comp_on) {
     uint16_t *zs = reinterpret_cast<uint16_t *>(lds);
-    z_prologue<8, 4>(a, false, a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
+    z_prologue<8, kTiledWaves>(a, false, a.zp_d, a.RZ, a.ks_stride_d, a.ks_d, a.RZ, ch, zs);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const int row = strips[q] * 16 + (lane & 15);
       if (a.r > 0) lowrank_epi<8>(d.U, a.r, a.Rp, row, zs, a.RZ, acc[q]);
       if (a.rs > 0) lowrank_epi<8>(d.Us, a.rs, a.Rsp, row, zs + a.Rp, a.RZ, acc[q]);
@@ -398,7 +426,7 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   }
   float *yp = a.ypart;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int row = strips[q] * 16 + (lane & 15);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -413,7 +441,7 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
 
 // grid.x = (upper bound of token tiles) * (I / 128), rounded up to 8
 template <int GPT>
-__global__ void __launch_bounds__(256, 1) tiled_gateup_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_gateup_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.I / kTileK;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
@@ -436,7 +464,7 @@ __global__ void __launch_bounds__(256, 1) tiled_gateup_kernel(FfnArgs a) {
 
 // grid.x = (upper bound of token tiles) * (H / 256), rounded up to 8
 template <int GPT>
-__global__ void __launch_bounds__(256, 1) tiled_down_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_down_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.H / 256;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
