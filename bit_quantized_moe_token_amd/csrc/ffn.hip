@@ -77,6 +77,18 @@ static int pick_ks(int P, int K) {
   return std::max(1, std::min(16, K / 1024));
 }
 
+// The down projection in wave tiles (lowrank_project_kernel, WT): many
+// pairs, no shared factors, at most four 16-column jobs, and a K long
+// enough to split over the grid.  Its K splits make about 1024 workgroups.
+static bool wave_tiles(const moeq_layer *L, int64_t P) {
+  const int Rp = (L->dims.r + 31) / 32 * 32;
+  return P > 256 && L->dims.rs == 0 && Rp > 0 && Rp / 16 <= 4 && L->dims.I >= 4096;
+}
+static int wave_tile_ks(const moeq_layer *L, int64_t P) {
+  const int64_t tiles = P / 64 + L->dims.E;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({(1024 + tiles - 1) / tiles, 8, L->dims.I / 1024}));
+}
+
 static int hblk_stride(const moeq_layer *L) { return (L->dims.I / 64 + 15) / 16 * 16; }
 
 // z_tok: the gate/up projection covers every (token, expert) pair (the
@@ -88,7 +100,7 @@ static Ws ws_plan(const moeq_layer *L, int T, int k, int splits, bool z_tok = fa
   const int RZ = Rp + Rsp;
   Ws w;
   w.ks_gu = pick_ks((int)PZ, L->dims.H);
-  w.ks_d = pick_ks((int)P, L->dims.I);
+  w.ks_d = wave_tiles(L, P) ? wave_tile_ks(L, P) : pick_ks((int)P, L->dims.I);
   size_t off = 0;
   w.zp_gu = off; off = al256(off + (size_t)w.ks_gu * PZ * 2 * RZ * 4);
   w.zp_d = off; off = al256(off + (size_t)w.ks_d * P * RZ * 4);
@@ -155,6 +167,7 @@ static moeq_status ffn_setup(const moeq_layer *L, const uint16_t *x, int32_t T, 
   a.z_tok = z_tok ? 1 : 0;
   a.ks_gu = w.ks_gu;
   a.ks_d = w.ks_d;
+  a.wt = wave_tiles(L, (int64_t)T * k) ? 1 : 0;
   a.ks_stride_gu = (int64_t)T * (z_tok ? D.E : k) * 2 * a.RZ;
   a.ks_stride_d = (int64_t)T * k * a.RZ;
   a.h = reinterpret_cast<uint16_t *>(wb + w.h);

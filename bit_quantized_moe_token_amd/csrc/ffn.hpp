@@ -37,6 +37,7 @@ struct FfnArgs {
   int32_t *dlead;   // [P] member mask of a down leader, 0 for the other pairs
   int64_t ks_stride_sh;
   int ks_gu, ks_d;  // K splits of the two projections
+  int wt;            // the down projection runs in wave tiles (see lowrank_project_kernel)
   int64_t ks_stride_gu, ks_stride_d;   // floats between consecutive splits
   uint16_t *h;      // [P][I] fp16: h * 2^(kNormTop - eb), eb per (pair, 64-row block of I)
   int8_t *hblk;     // [P][hblk_stride] eb (h_block_exp), I/64 used per row

@@ -34,8 +34,13 @@ namespace moeq {
 // no V and writes zero rows.
 // SH: the layer has shared factors (the group bookkeeping is compiled in
 // only then: its registers would cost the other layers occupancy).
-template <int NJ, bool ROUTE, bool SH>
+// WT (mode 1, many pairs, no shared factors): each wave owns one 16-pair
+// tile of a 64-pair chunk and the workgroup's whole K range (the K split
+// is grid.z alone), so the four waves read the same V fragments at about
+// the same time (one L2 read, the others from L1) and need no reduction.
+template <int NJ, bool ROUTE, bool SH, bool WT = false>
 __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mode, int njy, RouteOut ro) {
+  static_assert(!WT || (!SH && !ROUTE), "wave tiles: mode 1 without shared factors");
   __shared__ f32x4 s_part[4][NJ][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (mode != 1 && (int)blockIdx.y >= njy) {
@@ -59,10 +64,14 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
     ch.e = (int)blockIdx.x % a.E;
     sub = (int)blockIdx.x / a.E;
     ch.m0 = 0; ch.base = 0; ch.cnt = a.T;
+  } else if (WT) {
+    sub = wave;
+    if (!find_chunk<64>(a.offsets, a.E, blockIdx.x, &ch)) return;
   } else {
     sub = blockIdx.x % kSubPerChunk;
     if (!find_chunk(a.offsets, a.E, blockIdx.x / kSubPerChunk, &ch)) return;
   }
+  // (with WT a wave past the chunk's end leaves alone: no barrier follows)
   if (16 * sub >= ch.cnt) return;
   // the tile's pairs (rows past the count repeat the last one)
   const int mloc = std::min(16 * sub + (lane & 15), ch.cnt - 1);
@@ -129,7 +138,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   // zero z rows for the tile (by wave 0; shared columns are written by the
   // groups' leaders, and their readers mask uncompensated pairs)
   auto zero_rows = [&]() {
-    if (wave == 0)
+    if (WT || wave == 0)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = 16 * sub + 4 * (lane >> 4) + q;
@@ -166,7 +175,7 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   };
   const int nsteps = K / 32;
   const int z0 = (int)((int64_t)nsteps * blockIdx.z / KS), z1 = (int)((int64_t)nsteps * (blockIdx.z + 1) / KS);
-  const int s0 = z0 + (z1 - z0) * wave / 4, s1 = z0 + (z1 - z0) * (wave + 1) / 4;
+  const int s0 = WT ? z0 : z0 + (z1 - z0) * wave / 4, s1 = WT ? z1 : z0 + (z1 - z0) * (wave + 1) / 4;
   // no pair of the tile compensated (router-guided top-n): zero z rows, no
   // V loads; in mode 1 slice 0 still stores the tile's renormalised h
   if (!tile_comp) {
@@ -229,6 +238,20 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(FfnArgs a, int mod
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] += acc2[j][q];
+  }
+  if constexpr (WT) {
+    // the wave's own rows, no reduction
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 16 * sub + 4 * (lane >> 4) + q;
+      if (m < ch.cnt) {
+        const bool comp = (a.sorted_pairs[ch.base + m] % a.k) < a.n_comp;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (zcol[j] < a.Rp) zbase[zrow(m) * zstride + zcol[j]] = (comp && live[j]) ? acc[j][q] : 0.0f;
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s_part[wave][j][lane] = acc[j];
@@ -388,6 +411,17 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a, void *y) {
 }
 
 void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s) {
+  if (mode == 1 && a.wt) {
+    // wave tiles: all jobs of a 64-pair chunk in one workgroup
+    const dim3 grid(max_chunks(a.E, a.T, a.k, 64), 1, a.ks_d);
+    const RouteOut ro{};
+    switch (jobs) {
+      case 4: hipLaunchKernelGGL((lowrank_project_kernel<4, false, false, true>), grid, dim3(256), 0, s, a, 1, 1, ro); break;
+      case 2: hipLaunchKernelGGL((lowrank_project_kernel<2, false, false, true>), grid, dim3(256), 0, s, a, 1, 1, ro); break;
+      default: hipLaunchKernelGGL((lowrank_project_kernel<1, false, false, true>), grid, dim3(256), 0, s, a, 1, 1, ro); break;
+    }
+    return;
+  }
   dim3 grid(mode == 2 ? (a.T + 15) / 16 * a.E : max_chunks(a.E, a.T, a.k) * kSubPerChunk, jobs,
             mode != 1 ? a.ks_gu : a.ks_d);
   // two, four or eight jobs per workgroup when many tokens leave no K

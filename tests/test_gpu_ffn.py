@@ -21,6 +21,9 @@ CASES = {
     "prefill": ("prefill", dict(H=512, I=1792, T=1536)),
     # the int3 layer with as many tokens (where its default turns tiled)
     "decode_many": ("decode", dict(H=512, I=1792, T=1536)),
+    # many pairs and I >= 4096: the down projection runs in wave tiles
+    # (each wave a 16-pair tile of a 64-pair chunk, K split over the grid)
+    "prefill_wide": ("prefill", dict(H=512, I=4096, T=1024)),
     "finegrained": ("finegrained", {}),
     "bitplane": ("bitplane", dict(E=32, T=128)),
     # the largest expert count (256): experts with one or two pairs, chunk
@@ -76,7 +79,7 @@ def test_ffn_matches_oracle(case, seed):
     layers.check_y(y16.float().cpu().numpy(), ref, f"{case} seed {seed} fp16")
 
 
-@pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane", "shared_int"])
+@pytest.mark.parametrize("case", ["tiny", "finegrained", "bitplane", "shared_int", "prefill_wide"])
 def test_ffn_compensation_switch(case):
     """n_comp in {0, 1, k} against the oracle; n_comp = 0 equals the layer
     without factors bit for bit."""
@@ -88,7 +91,8 @@ def test_ffn_compensation_switch(case):
 
 
 @pytest.mark.parametrize("case,path", [("decode", PATH_STREAM), ("prefill", PATH_STREAM),
-                                       ("prefill", PATH_TILED), ("finegrained", PATH_AUTO)])
+                                       ("prefill", PATH_TILED), ("finegrained", PATH_AUTO),
+                                       ("prefill_wide", PATH_TILED), ("prefill_wide", PATH_STREAM)])
 def test_ffn_expert_reached_only_by_uncompensated_slots(case, path):
     """Router-guided top-n compensation with n_comp = 1 when one expert is
     every token's second choice: all of its pairs are uncompensated, so its
