@@ -314,9 +314,10 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
                                make_rsrc(du.codes, code_region_bytes(du))};
   // the low-rank epilogue's inputs (z rows for up to 64 columns from one
   // partial, and the first U operands) are requested before the K walk, so
-  // the epilogue does not wait for memory
+  // the epilogue does not wait for memory (z rows not with two groups per
+  // tile, whose decode state leaves no registers for them)
   const int zw = 2 * a.RZ;
-  const bool zpre = a.comp_on && a.ks_gu == 1 && zw <= 64 && a.rs == 0;
+  const bool zpre = GPT == 1 && a.comp_on && a.ks_gu == 1 && zw <= 64 && a.rs == 0;
   ZPre<8, kTiledWaves, 4> zp;
   if (zpre) z_preload<8, kTiledWaves, 4>(a.zp_gu, zw, zw, ch, zp);
   f16x8 ub[2];
