@@ -128,6 +128,21 @@ def test_rank0_bitwise_equals_uncompensated():
     assert torch.equal(y0, y1)
 
 
+def test_ffn_wave_tiles_uneven_k_split():
+    """Wave tiles whose K split does not divide the 32-column steps evenly
+    (I = 8320: 260 steps over 8 grid slices), on both paths, against the
+    oracle; and bit-identical on a repeat (fixed order of the partials)."""
+    cfg = configs.reduced(configs.get("prefill"), H=256, I=8320, T=1024)
+    orc = layers.oracle_layer(cfg, 0, cache_blocks=3 * cfg["E"])
+    dev = layers.device_layer(cfg, 0, orc)
+    x, logits = gen.gen_x(cfg, 0), gen.gen_logits(cfg, 0)
+    ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
+    for path in (PATH_TILED, PATH_STREAM):
+        y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=path)
+        layers.check_y(y.cpu().numpy(), ref, f"I=8320 path {path}")
+        assert torch.equal(y, _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=path))
+
+
 @pytest.mark.parametrize("case", ["decode", "finegrained"])
 def test_ffn_deterministic_and_split_invariant(case):
     cfg, orc, dev, x, logits = _setup(case)
