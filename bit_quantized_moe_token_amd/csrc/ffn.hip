@@ -18,16 +18,17 @@ struct Ws {
   int ks_gu, ks_d;
 };
 
-// Kernel path of one call.  Tiled: INT blocks, on average at least
-// tiled_min_pairs per expert (below that, streaming the weights once per
-// 32-token chunk is as fast or faster on a Mixtral-sized layer), shapes the tiled kernels cover (H a multiple of 256, 32-bit
-// element offsets of the activation rows, z rows that fit one activation
-// buffer); weight streaming otherwise.
+// Kernel path of one call.  Tiled: on average at least tiled_min_pairs per
+// expert (below that, streaming the weights once per 32-token chunk is as
+// fast or faster on a Mixtral-sized layer), shapes the tiled kernels cover
+// (H a multiple of 256, 32-bit element offsets of the activation rows and
+// byte offsets of a block's codes, z rows that fit one activation buffer);
+// weight streaming otherwise.  INT and bit-plane blocks alike.
 static bool tiled_fits(const moeq_layer *L, int T, int k) {
   const LayerDims &D = L->dims;
   const int64_t P = (int64_t)T * k;
   const int RZ = (D.r + 31) / 32 * 32 + (D.rs + 31) / 32 * 32;
-  return D.fmt == MOEQ_FMT_INT && D.H % 256 == 0 && D.I % kTileK == 0 &&
+  return D.H % 256 == 0 && D.I % kTileK == 0 && (int64_t)D.H * D.I / 2 < (1ll << 31) &&
          (int64_t)T * D.H < (1ll << 31) && P * D.I < (1ll << 31) && 2 * RZ <= kTileK + 8;
 }
 
@@ -36,8 +37,11 @@ static bool tiled_fits(const moeq_layer *L, int T, int k) {
 // T = 384) and on the fine-grained one (E = 64, k = 6, I = 1408: T = 1024);
 // 384 for int3 on the Mixtral-sized layer (T = 1536), whose fields cost the
 // tiled decode more; layers with any block below 4 bits take the larger
-// figure.
+// figure.  Bit-plane layers: 192, between the points measured on the
+// 128-expert layer (k = 8, H = 2048, I = 768, q in {2, 3, 4}): streaming
+// 6% faster at 128 pairs per expert (T = 2048), tiled 5% faster at 256.
 static int64_t tiled_min_pairs(const moeq_layer *L) {
+  if (L->dims.fmt == MOEQ_FMT_BITPLANE) return 192;
   for (uint8_t b : L->bits)
     if (b != 4) return 384;
   return 96;

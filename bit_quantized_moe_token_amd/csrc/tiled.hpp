@@ -75,6 +75,25 @@ __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
   return pack_b(p[0], p[1], p[2], p[3]);
 }
 
+// Bit-plane strip of one 128-column tile: the top q planes (one dword per
+// plane; pl[u] = plane 3 - u, as plane_sel expects) and the lane's row LUT
+// byte-split for the permute lookups (the 2^q low bytes in 2^q / 4 dwords,
+// then the high bytes).  The LUT group is the tile (128 columns).
+template <int Q>
+struct PTile {
+  uint32_t w[Q];
+  uint32_t L[1 << (Q - 1)];
+};
+
+template <int B, bool PLANE>
+struct TileOf {
+  using type = TTile<B>;
+};
+template <int Q>
+struct TileOf<Q, true> {
+  using type = PTile<Q>;
+};
+
 // ---- LDS stages.  A stage holds one 128-column tile: the activation tile
 // (128 token rows x 256 B, 16-byte slots XOR-swizzled by row so that the
 // MFMA operand reads are bank-conflict free), the packed codes of the
@@ -87,15 +106,22 @@ __device__ __forceinline__ f16x8 tdecode(const TTile<B> &tt, int j) {
 // (explicit waits: the compiler does not track DMA writes into LDS).
 // Staging the same loads through registers (buffer loads, then LDS
 // stores) measured slower.
+// Bit-plane layers use the same stage with a 1 KiB slot per wave for the
+// two strips' LUTs (16 rows x 2^q fp16, up to 512 bytes per strip) in place
+// of the scales and zeros; that leaves room for two stages, not three.
 constexpr int kTABytes = kTM * 256;
 constexpr int kTBBytes = 16 * 1024;
-constexpr int kTMetaBytes = kTiledWaves * 512;        // per wave: 64 lanes x 2 dword slots
-constexpr int kTStageBytes = kTABytes + kTBBytes + kTMetaBytes;
-constexpr int kTStages = 3;
-constexpr size_t kTiledLdsBytes = (size_t)kTStages * kTStageBytes;
-// dynamic LDS of a tiled launch: the stages, then the gate/up rows' x
-// exponents and pair ids
-constexpr size_t kTiledLdsLaunch = kTiledLdsBytes + 2 * kTM * 4;
+template <bool PLANE>
+struct TStages {
+  static constexpr int kMeta = PLANE ? 1024 : 512;   // per wave (INT: 64 lanes x 2 dword slots)
+  static constexpr int kBytes = kTABytes + kTBBytes + kTiledWaves * kMeta;
+  static constexpr int kN = PLANE ? 2 : 3;
+  static constexpr size_t kLds = (size_t)kN * kBytes;
+  // dynamic LDS of a gate/up launch: the stages, then the rows' x
+  // exponents and pair ids
+  static constexpr size_t kLaunchGU = kLds + 2 * kTM * 4;
+};
+static_assert(TStages<false>::kLaunchGU <= 160 * 1024 && TStages<true>::kLaunchGU <= 160 * 1024, "LDS");
 
 // DMA operations per strip per tile: one 16-byte transfer for 4-bit codes,
 // else one 4-byte transfer per code dword.
@@ -112,6 +138,50 @@ __device__ __forceinline__ void dma_codes(__amdgpu_buffer_rsrc_t codes, int stri
       const WordOff o = tile_word_off<B>(strip, t, e, n_kt);
       lds_dma_buf<4>(codes, o.lane, o.uni, dst + 256 * e);
     }
+  }
+}
+
+// Bit-plane codes: one 4-byte transfer per plane; plane u of lane l of
+// tile t sits at u * plane_bytes + code_offset(strip, t, l, n_kt, 4).
+template <int Q>
+__device__ __forceinline__ void dma_planes(__amdgpu_buffer_rsrc_t codes, uint32_t plane_bytes, int strip, int t,
+                                           int n_kt, uint8_t *dst) {
+  const int lane = threadIdx.x & 63;
+  const int g4 = t >> 2, tl = t & 3;
+  const int c = std::min(4, n_kt - 4 * g4);
+  const uint32_t uni = (uint32_t)strip * n_kt * 256 + (uint32_t)g4 * 1024 + (uint32_t)tl * 4;
+#pragma unroll
+  for (int u = 0; u < Q; ++u) lds_dma_buf<4>(codes, (uint32_t)(lane * c * 4), uni + (uint32_t)u * plane_bytes, dst + 256 * u);
+}
+
+template <int Q>
+__device__ __forceinline__ void lds_planes(const uint8_t *src, PTile<Q> &tt) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < Q; ++u) tt.w[u] = *reinterpret_cast<const uint32_t *>(src + 256 * u + 4 * lane);
+}
+
+// The lane's row LUT (row lane % 16 of a strip's 16 x 2^q table at src),
+// byte-split.
+template <int Q>
+__device__ __forceinline__ void lds_lut(const uint8_t *src, PTile<Q> &tt) {
+  constexpr int NQ = 1 << Q;
+  const uint8_t *row = src + (threadIdx.x & 15) * 2 * NQ;
+  uint32_t v[NQ / 2];
+  if constexpr (Q == 2) {
+    const u32x2 a = *reinterpret_cast<const u32x2 *>(row);
+    v[0] = a[0]; v[1] = a[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NQ / 8; ++i) {
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(row + 16 * i);
+      v[4 * i] = a[0]; v[4 * i + 1] = a[1]; v[4 * i + 2] = a[2]; v[4 * i + 3] = a[3];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NQ / 4; ++m) {
+    tt.L[m] = __builtin_amdgcn_perm(v[2 * m + 1], v[2 * m], 0x06040200u);
+    tt.L[NQ / 4 + m] = __builtin_amdgcn_perm(v[2 * m + 1], v[2 * m], 0x07050301u);
   }
 }
 
@@ -137,10 +207,17 @@ __device__ __forceinline__ f16x8 tlds_a(const uint8_t *abuf, int s, int j) {
 // The strips of wave w: q = 0 from block d0 (bits B0), q = 1 from d1 (bits
 // B1); their codes sit at 1 KiB slots 2 w + q of the stage, their scales
 // and zeros in lanes 16 q .. 16 q + 15 of the wave's metadata slots (lanes
-// 32 .. 63 repeat lanes 0 .. 31).
-template <int B0, int B1, int GPT>
+// 32 .. 63 repeat lanes 0 .. 31).  Bit-plane (PLANE; B0, B1 the committed
+// q): plane u of a strip at 256 u of its slot, the strips' LUTs at 0 and
+// 512 of the wave's metadata slot (lanes 0 .. 31 move strip 0's table,
+// 32 .. 63 strip 1's, 16 bytes each).
+template <int B0, int B1, int GPT, bool PLANE = false>
 struct TKLoop {
-  static constexpr int kDma = 4 + dma_ops(B0) + dma_ops(B1) + 2;   // DMA ops per tile per wave
+  using St = TStages<PLANE>;
+  using Tile0 = typename TileOf<B0, PLANE>::type;
+  using Tile1 = typename TileOf<B1, PLANE>::type;
+  // DMA ops per tile per wave
+  static constexpr int kDma = PLANE ? 4 + B0 + B1 + 1 : 4 + dma_ops(B0) + dma_ops(B1) + 2;
   const BlockDesc &d0, &d1;
   const int *strips;
   int n_kt, wave;
@@ -162,28 +239,46 @@ struct TKLoop {
       lds_dma_buf<16>(ra, 2u * (rowoff[i] + 8u * c), (uint32_t)t * (kTileK * 2), a + (16 * wave + 4 * i) * 256);
     }
     uint8_t *b = a + kTABytes + 2 * wave * 1024;
-    dma_codes<B0>(rc0, strips[0], t, n_kt, b);
-    dma_codes<B1>(rc1, strips[1], t, n_kt, b + 1024);
-    // lane l: strip q = (l / 16) % 2, row l % 16
-    const int q = (lane >> 4) & 1;
-    const BlockDesc &dq = q == 0 ? d0 : d1;
-    const uint64_t mi = meta_index(q == 0 ? strips[0] : strips[1], t, lane & 15, 0, n_kt, GPT);
-    uint8_t *m = a + kTABytes + kTBBytes + wave * 512;
-    lds_dma<2 * GPT>(dq.scales + mi, m);       // dword slot per lane
-    lds_dma<GPT>(dq.zeros + mi, m + 256);      // zero-extended dword slot per lane
+    if constexpr (PLANE) {
+      dma_planes<B0>(rc0, (uint32_t)d0.plane_bytes, strips[0], t, n_kt, b);
+      dma_planes<B1>(rc1, (uint32_t)d1.plane_bytes, strips[1], t, n_kt, b + 1024);
+      // strip q's table: 16 rows x 2^q fp16 = 2 * 2^q 16-byte pieces
+      const int q = lane >> 5, i = lane & 31;
+      const int nq = q == 0 ? (1 << B0) : (1 << B1);
+      const uint16_t *src = (q == 0 ? d0.lut : d1.lut) + lut_index(strips[q], t, 0, 0, n_kt, nq) +
+                            8 * std::min(i, 2 * nq - 1);
+      lds_dma<16>(src, a + kTABytes + kTBBytes + wave * St::kMeta);
+    } else {
+      dma_codes<B0>(rc0, strips[0], t, n_kt, b);
+      dma_codes<B1>(rc1, strips[1], t, n_kt, b + 1024);
+      // lane l: strip q = (l / 16) % 2, row l % 16
+      const int q = (lane >> 4) & 1;
+      const BlockDesc &dq = q == 0 ? d0 : d1;
+      const uint64_t mi = meta_index(q == 0 ? strips[0] : strips[1], t, lane & 15, 0, n_kt, GPT);
+      uint8_t *m = a + kTABytes + kTBBytes + wave * St::kMeta;
+      lds_dma<2 * GPT>(dq.scales + mi, m);       // dword slot per lane
+      lds_dma<GPT>(dq.zeros + mi, m + 256);      // zero-extended dword slot per lane
+    }
   }
 
   // the codes, scales and zeros of the wave's strips from the stage at sb
-  __device__ __forceinline__ void load_codes(uint32_t sb, TTile<B0> &t0, TTile<B1> &t1) const {
+  __device__ __forceinline__ void load_codes(uint32_t sb, Tile0 &t0, Tile1 &t1) const {
     const int r = threadIdx.x & 15;
     const uint8_t *b = lds + sb + kTABytes + 2 * wave * 1024;
-    const uint8_t *m = lds + sb + kTABytes + kTBBytes + wave * 512;
-    lds_codes<B0>(b, t0);
-    lds_codes<B1>(b + 1024, t1);
-    const uint32_t *sc = reinterpret_cast<const uint32_t *>(m);
-    const uint32_t *zz = reinterpret_cast<const uint32_t *>(m + 256);
-    t0.sc = sc[r]; t1.sc = sc[16 + r];
-    t0.zz = zz[r]; t1.zz = zz[16 + r];
+    const uint8_t *m = lds + sb + kTABytes + kTBBytes + wave * St::kMeta;
+    if constexpr (PLANE) {
+      lds_planes<B0>(b, t0);
+      lds_planes<B1>(b + 1024, t1);
+      lds_lut<B0>(m, t0);
+      lds_lut<B1>(m + 512, t1);
+    } else {
+      lds_codes<B0>(b, t0);
+      lds_codes<B1>(b + 1024, t1);
+      const uint32_t *sc = reinterpret_cast<const uint32_t *>(m);
+      const uint32_t *zz = reinterpret_cast<const uint32_t *>(m + 256);
+      t0.sc = sc[r]; t1.sc = sc[16 + r];
+      t0.zz = zz[r]; t1.zz = zz[16 + r];
+    }
   }
 
   // activation fragments of step j of the tile in the stage at sb
@@ -193,9 +288,14 @@ struct TKLoop {
     for (int s = 0; s < NT; ++s) av[s] = tlds_a(lds + sb, s, j);
   }
 
-  __device__ __forceinline__ static void decode(const TTile<B0> &t0, const TTile<B1> &t1, int j, f16x8 *w) {
-    w[0] = tdecode<B0, GPT>(t0, j);
-    w[1] = tdecode<B1, GPT>(t1, j);
+  __device__ __forceinline__ static void decode(const Tile0 &t0, const Tile1 &t1, int j, f16x8 *w) {
+    if constexpr (PLANE) {
+      w[0] = plane_bop<B0>(t0.w, j, t0.L);
+      w[1] = plane_bop<B1>(t1.w, j, t1.L);
+    } else {
+      w[0] = tdecode<B0, GPT>(t0, j);
+      w[1] = tdecode<B1, GPT>(t1, j);
+    }
   }
 
   // the two MFMAs of token sub-tile s of a step
@@ -211,7 +311,7 @@ struct TKLoop {
   // weights decoded into wn between them.
   template <int NT>
   __device__ __forceinline__ void step(f16x8 *av, const f16x8 *wc, f16x8 *wn, f32x4 (*acc)[NT], uint32_t sn,
-                                       int jn, const TTile<B0> &t0, const TTile<B1> &t1) const {
+                                       int jn, const Tile0 &t0, const Tile1 &t1) const {
     decode(t0, t1, jn, wn);
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
@@ -234,18 +334,20 @@ struct TKLoop {
   // and its weights decoded.  Tile t + 1's stage is opened (wait for its
   // transfers, barrier) before the last step of tile t, whose weights are
   // already decoded, so that step reads tile t + 1's codes and first
-  // activation fragments and decodes its first step.  Transfers run three
-  // tiles ahead; tile t + 3 goes into tile t's stage once every wave has
-  // passed that barrier with all its reads of the stage completed.
+  // activation fragments and decodes its first step.  With N stages
+  // transfers run N tiles ahead; tile t + N goes into tile t's stage once
+  // every wave has passed that barrier with all its reads of the stage
+  // completed.
   template <int NT>
   __device__ __forceinline__ void run(f32x4 (*acc)[NT]) const {
+    constexpr int N = St::kN;
     issue(0, 0);
-    issue(std::min(1, n_kt - 1), kTStageBytes);
-    issue(std::min(2, n_kt - 1), 2 * kTStageBytes);
-    vm_wait<2 * kDma>();
+    issue(std::min(1, n_kt - 1), St::kBytes);
+    if constexpr (N == 3) issue(std::min(2, n_kt - 1), 2 * St::kBytes);
+    vm_wait<(N - 1) * kDma>();
     __builtin_amdgcn_s_barrier();
-    TTile<B0> t0;
-    TTile<B1> t1;
+    Tile0 t0;
+    Tile1 t1;
     f16x8 av[NT], w0[2], w1[2];
     load_codes(0, t0, t1);
     load_a<NT>(0, 0, av);
@@ -258,10 +360,10 @@ struct TKLoop {
       step<NT>(av, w0, w1, acc, sb, 3, t0, t1);
       // open tile t + 1 (on the last tile: a stage of re-read data whose
       // values go unused)
-      lgkm_vm_wait<kDma>();
+      lgkm_vm_wait<(N - 2) * kDma>();
       __builtin_amdgcn_s_barrier();
-      const uint32_t sn = sb == 2 * kTStageBytes ? 0u : sb + kTStageBytes;
-      issue(std::min(t + 3, n_kt - 1), sb);
+      const uint32_t sn = sb == (N - 1) * St::kBytes ? 0u : sb + St::kBytes;
+      issue(std::min(t + N, n_kt - 1), sb);
       load_codes(sn, t0, t1);
       __builtin_amdgcn_sched_barrier(0);
       step<NT>(av, w1, w0, acc, sn, 0, t0, t1);
@@ -278,9 +380,17 @@ struct TKLoop {
 // XCD a contiguous run of tiles.
 __device__ __forceinline__ int xcd_tile(int b, int n) { return (b & 7) * (n >> 3) + (b >> 3); }
 
+// Buffer resource over a block's codes: the INT code region, or the top B
+// bit-planes (stored top plane first, plane_bytes apart).
+template <int B, bool PLANE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t code_rsrc(const BlockDesc &d) {
+  if constexpr (PLANE) return make_rsrc(d.codes, (uint32_t)B * (uint32_t)d.plane_bytes);
+  else return make_rsrc(d.codes, code_region_bytes(d));
+}
+
 // gate/up: wave w owns I rows nt*128 + 16 w + [0, 16) of gate (q = 0) and
 // up (q = 1), for all 128 tokens of the tile.
-template <int BG, int BU, int GPT>
+template <int BG, int BU, int GPT, bool PLANE>
 __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -302,7 +412,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const TKLoop<BG, BU, GPT> kl{dg,
+  const TKLoop<BG, BU, GPT, PLANE> kl{dg,
                                du,
                                strips,
                                a.H / kTileK,
@@ -310,8 +420,8 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
                                rowoff,
                                lds,
                                make_rsrc(a.xn, (uint32_t)a.T * (uint32_t)a.H * 2u),
-                               make_rsrc(dg.codes, code_region_bytes(dg)),
-                               make_rsrc(du.codes, code_region_bytes(du))};
+                                      code_rsrc<BG, PLANE>(dg),
+                                      code_rsrc<BU, PLANE>(du)};
   // the low-rank epilogue's inputs (z rows for up to 64 columns from one
   // partial, and the first U operands) are requested before the K walk, so
   // the epilogue does not wait for memory (z rows not with two groups per
@@ -327,7 +437,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
                                  : pack_b(0, 0, 0, 0);
   kl.template run<8>(acc);
   // acc holds W x~ (x~ = x 2^K, the normalised rows), as do the z rows
-  int *s_kx = reinterpret_cast<int *>(lds + kTiledLdsBytes);
+  int *s_kx = reinterpret_cast<int *>(lds + TStages<PLANE>::kLds);
   int *s_p = s_kx + kTM;
   if (threadIdx.x < kTM) {
     s_kx[threadIdx.x] = kreg;
@@ -392,7 +502,7 @@ __device__ __forceinline__ void tiled_gateup_body(const FfnArgs &a, const Chunk 
 }
 
 // down: wave w owns H rows nt*256 + 32 w + [0, 32).
-template <int BD, int GPT>
+template <int BD, int GPT, bool PLANE>
 __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &ch, int nt, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -410,8 +520,8 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[q][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.codes, code_region_bytes(d));
-  const TKLoop<BD, BD, GPT> kl{d, d, strips, a.I / kTileK, wave, rowoff, lds,
+  const __amdgpu_buffer_rsrc_t rc = code_rsrc<BD, PLANE>(d);
+  const TKLoop<BD, BD, GPT, PLANE> kl{d, d, strips, a.I / kTileK, wave, rowoff, lds,
                                make_rsrc(a.hn, (uint32_t)a.P * (uint32_t)a.I * 2u), rc, rc};
   kl.template run<8>(acc);
   if (a.comp_on) {
@@ -440,8 +550,10 @@ __device__ __forceinline__ void tiled_down_body(const FfnArgs &a, const Chunk &c
   }
 }
 
-// grid.x = (upper bound of token tiles) * (I / 128), rounded up to 8
-template <int GPT>
+// grid.x = (upper bound of token tiles) * (I / 128), rounded up to 8.
+// PLANE: bit-plane blocks (GPT = 1, one LUT per 128-column tile), the
+// committed q of each block in place of b.
+template <int GPT, bool PLANE>
 __global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_gateup_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.I / kTileK;
@@ -451,20 +563,20 @@ __global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_gateup_kernel(FfnAr
   if (!find_chunk<kTM>(a.offsets, a.E, mt, &ch)) return;
   const int bg = a.desc[3 * ch.e].bits, bu = a.desc[3 * ch.e + 1].bits;
   switch (bg * 4 + bu) {
-    case 2 * 4 + 2: tiled_gateup_body<2, 2, GPT>(a, ch, nt, tl_lds); break;
-    case 2 * 4 + 3: tiled_gateup_body<2, 3, GPT>(a, ch, nt, tl_lds); break;
-    case 2 * 4 + 4: tiled_gateup_body<2, 4, GPT>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 2: tiled_gateup_body<3, 2, GPT>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 3: tiled_gateup_body<3, 3, GPT>(a, ch, nt, tl_lds); break;
-    case 3 * 4 + 4: tiled_gateup_body<3, 4, GPT>(a, ch, nt, tl_lds); break;
-    case 4 * 4 + 2: tiled_gateup_body<4, 2, GPT>(a, ch, nt, tl_lds); break;
-    case 4 * 4 + 3: tiled_gateup_body<4, 3, GPT>(a, ch, nt, tl_lds); break;
-    default: tiled_gateup_body<4, 4, GPT>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 2: tiled_gateup_body<2, 2, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 3: tiled_gateup_body<2, 3, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 2 * 4 + 4: tiled_gateup_body<2, 4, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 2: tiled_gateup_body<3, 2, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 3: tiled_gateup_body<3, 3, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 3 * 4 + 4: tiled_gateup_body<3, 4, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 4 * 4 + 2: tiled_gateup_body<4, 2, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 4 * 4 + 3: tiled_gateup_body<4, 3, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    default: tiled_gateup_body<4, 4, GPT, PLANE>(a, ch, nt, tl_lds); break;
   }
 }
 
 // grid.x = (upper bound of token tiles) * (H / 256), rounded up to 8
-template <int GPT>
+template <int GPT, bool PLANE>
 __global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_down_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   const int n_nt = a.H / 256;
@@ -473,12 +585,10 @@ __global__ void __launch_bounds__(64 * kTiledWaves, 1) tiled_down_kernel(FfnArgs
   Chunk ch;
   if (!find_chunk<kTM>(a.offsets, a.E, mt, &ch)) return;
   switch (a.desc[3 * ch.e + 2].bits) {
-    case 2: tiled_down_body<2, GPT>(a, ch, nt, tl_lds); break;
-    case 3: tiled_down_body<3, GPT>(a, ch, nt, tl_lds); break;
-    default: tiled_down_body<4, GPT>(a, ch, nt, tl_lds); break;
+    case 2: tiled_down_body<2, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    case 3: tiled_down_body<3, GPT, PLANE>(a, ch, nt, tl_lds); break;
+    default: tiled_down_body<4, GPT, PLANE>(a, ch, nt, tl_lds); break;
   }
 }
-
-
 
 }  // namespace moeq

@@ -374,7 +374,10 @@ typedef enum {
                            of up to 32 of an expert's tokens (16-row MFMA
                            tiles)                                              */
   /* 2 is reserved (MOEQ_ERR_UNSUPPORTED)                                     */
-  MOEQ_PATH_TILED = 3   /* LDS-tiled grouped GEMM for many tokens per expert   */
+  MOEQ_PATH_TILED = 3   /* LDS-tiled grouped GEMM for many tokens per expert
+                           (INT and bit-plane blocks; MOEQ_ERR_UNSUPPORTED
+                           when H is not a multiple of 256, or the rows,
+                           codes or compensator width exceed its limits)    */
 } moeq_path;
 
 typedef struct {

@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 CFG = configs.reduced(configs.get("bitplane"), E=32, T=128)
 
 
-def _run(dev, x, logits, n_comp):
+def _run(dev, x, logits, n_comp, path=0):
     from bit_quantized_moe_token_amd import moeq
     rt = moeq.route(torch.from_numpy(logits).cuda(), CFG["k"])
-    y = moeq.expert_ffn(dev, torch.from_numpy(x).cuda(), rt, n_comp, out_dtype=torch.float32)
+    y = moeq.expert_ffn(dev, torch.from_numpy(x).cuda(), rt, n_comp, out_dtype=torch.float32, path=path)
     torch.cuda.synchronize()
     return y
 
@@ -53,7 +53,10 @@ def test_commit_changes_bitwidth(setup):
             assert dev.committed_bits(e, b) == bits1[e, b]
     y1 = _run(dev, x, logits, n_comp)
     orc1 = layers.oracle_layer(CFG, 0, cache_blocks=3 * E, bits=bits1)
-    layers.check_y(y1.cpu().numpy(), layers.oracle_y(orc1, CFG, x, logits, n_comp), "committed bits")
+    ref1 = layers.oracle_y(orc1, CFG, x, logits, n_comp)
+    layers.check_y(y1.cpu().numpy(), ref1, "committed bits")
+    # the tiled path reads the same committed planes and tables
+    layers.check_y(_run(dev, x, logits, n_comp, path=3).cpu().numpy(), ref1, "committed bits, tiled")
     # committed bytes follow the planes and tables now read
     N_K = {0: CFG["I"] * CFG["H"], 1: CFG["I"] * CFG["H"], 2: CFG["H"] * CFG["I"]}
     want = bytes0 + sum(N_K[b] * (int(bits1[e, b]) - int(bits0[e, b])) // 8 +
@@ -86,7 +89,10 @@ def test_paged_out_planes_are_not_read(setup):
     torch.cuda.synchronize()
     assert torch.equal(_run(dev, x, logits, n_comp), y2)
     orc2 = layers.oracle_layer(CFG, 0, cache_blocks=3 * E, bits=bits2)
-    layers.check_y(y2.cpu().numpy(), layers.oracle_y(orc2, CFG, x, logits, n_comp), "q=2 block")
+    ref2 = layers.oracle_y(orc2, CFG, x, logits, n_comp)
+    layers.check_y(y2.cpu().numpy(), ref2, "q=2 block")
+    # nor does the tiled path read them
+    layers.check_y(_run(dev, x, logits, n_comp, path=3).cpu().numpy(), ref2, "q=2 block, tiled")
     for view, host in saved:                            # paged back in, then committed
         view.copy_(host.cuda())
     dev.commit_bits(e, b, 4, _lut(e, b, 4))

@@ -30,6 +30,10 @@ CASES = {
     # lookup over four 64-lane passes, routing with E = 256
     "many_experts": ("finegrained", dict(E=256, k=8, T=48, H=256, I=256)),
     "many_experts_bitplane": ("bitplane", dict(E=256, T=40, H=256, I=256)),
+    # bit-plane blocks with many tokens per expert (256 pairs on average:
+    # full and partial 128-token tiles), a ragged last group of K tiles in
+    # the down projection (I = 768: 6 tiles)
+    "bitplane_wide": ("bitplane", dict(E=16, T=512, H=512, I=768)),
     # shared factors on an INT layer (groups of 4 of 16 experts, so a
     # token's six experts often share groups) whose low-rank terms are a
     # large part of the output (factors N(0, 0.05)); two of six slots
@@ -175,11 +179,14 @@ def test_ffn_zero_input_and_few_tokens():
         layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, sub, x[:T], logits[:T], cfg["k"]), f"T={T}")
 
 
-# ---- tiled path (many tokens per expert): forced on every INT workload,
+# ---- tiled path (many tokens per expert): forced on every workload,
 # including one token tile per expert (decode), mixed 2/3/4-bit blocks with
-# group 64 and an odd, ragged K-tile count (fine-grained: I = 1408 = 11 tiles)
+# group 64 and an odd, ragged K-tile count (fine-grained: I = 1408 = 11
+# tiles), and bit-plane blocks at mixed committed q with shared factors
+# (one or two pairs per expert, and 256)
 
-@pytest.mark.parametrize("case", ["tiny", "decode", "prefill", "finegrained", "shared_int"])
+@pytest.mark.parametrize("case", ["tiny", "decode", "prefill", "finegrained", "shared_int", "bitplane",
+                                  "many_experts_bitplane", "bitplane_wide"])
 def test_ffn_tiled_path_matches_oracle(case):
     cfg, orc, dev, x, logits = _setup(case)
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"])
@@ -265,8 +272,42 @@ def test_default_path_boundary():
     assert _gateup_kernel_run(dev, tiny, gen.gen_x(tiny, 0), gen.gen_logits(tiny, 0)) == "gateup_stream"
 
 
-def test_ffn_tiled_unsupported_for_bitplane():
+def test_default_path_boundary_bitplane():
+    """A bit-plane layer takes the tiled path from an average of 192 pairs
+    per expert (E = 16, k = 8, I = 1536: T = 384; its tiled grid has 468
+    workgroups) and streams at 188 (T = 376)."""
+    cfg = configs.reduced(configs.get("bitplane"), E=16, T=384, H=512, I=1536)
+    dev = layers.device_layer(cfg, 0)
+    x, logits = gen.gen_x(cfg, 0), gen.gen_logits(cfg, 0)
+    assert cfg["T"] * cfg["k"] == 192 * cfg["E"]
+    assert _gateup_kernel_run(dev, cfg, x, logits) == "gateup_tiled"
+    c188 = dict(cfg, T=376)
+    assert _gateup_kernel_run(dev, c188, x[:376].copy(), logits[:376].copy()) == "gateup_stream"
+
+
+def test_ffn_tiled_bitplane_deterministic_and_permutation():
+    """The tiled bit-plane path is bit-identical on a repeat and under a
+    permutation of the tokens (each token's output is its own sum in slot
+    order, whatever tile its pairs land in)."""
+    cfg, orc, dev, x, logits = _setup("bitplane_wide")
+    y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED)
+    assert torch.equal(y, _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32, path=PATH_TILED))
+    perm = np.random.default_rng(11).permutation(cfg["T"])
+    yp = _run(dev, cfg, x[perm].copy(), logits[perm].copy(), cfg["n_comp"], out_dtype=torch.float32,
+              path=PATH_TILED)
+    assert torch.equal(yp, y[torch.from_numpy(perm).cuda()])
+
+
+def test_ffn_tiled_rejects_unsupported_shape():
+    """The tiled kernels need H to be a multiple of 256 (two-strip output
+    tiles of the down projection); a forced tiled call on H = 384 is
+    rejected before anything runs, and the default path streams."""
     from bit_quantized_moe_token_amd import moeq
-    cfg, orc, dev, x, logits = _setup("bitplane")
+    cfg = configs.reduced(configs.get("tiny"), H=384, T=16)
+    orc = layers.oracle_layer(cfg, 0, cache_blocks=3 * cfg["E"])
+    dev = layers.device_layer(cfg, 0, orc)
+    x, logits = gen.gen_x(cfg, 0), gen.gen_logits(cfg, 0)
     with pytest.raises(moeq.MoeqError):
         _run(dev, cfg, x, logits, cfg["n_comp"], path=PATH_TILED)
+    y = _run(dev, cfg, x, logits, cfg["n_comp"], out_dtype=torch.float32)
+    layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"]), "H=384 default")

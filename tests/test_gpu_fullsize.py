@@ -24,7 +24,7 @@ def _sample_cols(H, n, seed):
     return np.array(sorted(cols))
 
 
-def _run_full(name, tokens, n_cols, seed=0):
+def _run_full(name, tokens, n_cols, seed=0, path=0):
     from bit_quantized_moe_token_amd import moeq
     cfg = configs.get(name)
     x = gen.gen_x(cfg, seed)
@@ -32,7 +32,7 @@ def _run_full(name, tokens, n_cols, seed=0):
     dev = layers.device_layer(cfg, seed)
     xd = torch.from_numpy(x).cuda()
     rt = moeq.route(torch.from_numpy(logits).cuda(), cfg["k"])
-    y = moeq.expert_ffn(dev, xd, rt, cfg["n_comp"], out_dtype=torch.float16)
+    y = moeq.expert_ffn(dev, xd, rt, cfg["n_comp"], out_dtype=torch.float16, path=path)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
     del dev
@@ -41,7 +41,7 @@ def _run_full(name, tokens, n_cols, seed=0):
     orc = layers.oracle_layer(cfg, seed, cache_blocks=2 * cfg["E"])
     ref = layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"], tokens=tokens, cols=cols)
     rel, fro = layers.check_y(y[np.ix_(tokens, cols)], ref, name)
-    print(f"{name} full size, {len(tokens)} tokens x {len(cols)} columns: "
+    print(f"{name} full size (path {path}), {len(tokens)} tokens x {len(cols)} columns: "
           f"max|err|/rms {rel:.2e}  fro {fro:.2e}")
 
 
@@ -68,3 +68,12 @@ def test_bitplane_full_size_sampled():
     T = configs.get("bitplane")["T"]
     tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 6).astype(int)]))
     _run_full("bitplane", tokens, 256)
+
+
+@pytest.mark.timeout(600)
+def test_bitplane_full_size_sampled_tiled():
+    """The same bit-plane layer on the tiled path (forced): 128-token tiles
+    of the bit-plane blocks at every committed q, shared factors."""
+    T = configs.get("bitplane")["T"]
+    tokens = np.unique(np.concatenate([[0, 2, T - 2], np.linspace(0, T - 1, 5).astype(int)]))
+    _run_full("bitplane", tokens, 192, path=3)
