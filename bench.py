@@ -740,6 +740,21 @@ def main():
                 hbm_frac=oalg["bytes"] / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_frac=oalg["flops"] / (oms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
                 weight_copies=R, kernels=ok)
+            if short == "bitplane":
+                # the same bit-plane layer with many tokens per expert (4096
+                # tokens, 256 pairs per expert on average): the default path
+                # is then the tiled one
+                pcfg = dict(ocfg, T=4096, name=ocfg["name"].replace("_t512_", "_t4096_"))
+                pms, pprof, palg = run_workload(pcfg, olayers, args.seed, max(10, args.steps // 10),
+                                                max(5, args.warmup // 4), args.path, graph=args.graph,
+                                                fused=not args.no_fused)
+                out["other_configs"]["bitplane_prefill"] = dict(
+                    workload=pcfg["name"], ms_per_step=pms, tokens_s=pcfg["T"] / (pms * 1e-3),
+                    alg_bytes=palg["bytes"], alg_flops=palg["flops"],
+                    tflops=palg["flops"] / (pms * 1e-3) / 1e12,
+                    mfma_frac=palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                    weight_copies=R,
+                    kernels={n: dict(launches=c, avg_us=1e3 * t / max(c, 1)) for n, (c, t) in pprof.items()})
             del olayers
             torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_extra:

@@ -426,10 +426,14 @@ void launch_lowrank_project(const FfnArgs &a, int mode, int jobs, hipStream_t s)
             mode != 1 ? a.ks_gu : a.ks_d);
   // two, four or eight jobs per workgroup when many tokens leave no K
   // split (the activation re-reads dominate; fewer jobs keep enough
-  // workgroups); the job count is always even
+  // workgroups); the job count is always even.  Four jobs in one workgroup
+  // when there are just four: on the down side only (bit-plane layer with
+  // rank 8 + shared 32: 24.6 -> 23.5 us at 512 tokens, 101 -> 72 us at
+  // 4096; on the gate/up side the fine-grained layer's projection went
+  // from 16.0 to 17.5 us)
   int nj = 1;
   if (a.P > 256 && grid.z == 1 && grid.y % 8 == 0) nj = 8;
-  else if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && grid.y >= 8) nj = 4;
+  else if (a.P > 256 && grid.z == 1 && grid.y % 4 == 0 && (grid.y >= 8 || mode == 1)) nj = 4;
   else if (a.P > 256 && grid.z == 1 && grid.y % 2 == 0) nj = 2;
   grid.y /= nj;
   const int njy = (int)grid.y;

@@ -124,3 +124,50 @@ def test_fit_full_size_block():
     assert res < tot
     assert tot - res >= 0.93 * captured_opt
     assert tot - res <= captured_opt * (1 + 1e-6)
+
+
+def test_ffn_with_device_fitted_factors():
+    """The tiny layer with its rank-16 compensators fitted on the device
+    (moeq_fit_lowrank, as the benchmark builds that layer): every block's
+    fitted factors strictly reduce the Frobenius norm of its RTN residual
+    (the compensator's defining property, MiLo abstract), and the routed
+    layer packed with them matches the oracle evaluated with the same
+    factors (the oracle's own quantization of the same fp16 weights)."""
+    from bit_quantized_moe_token_amd import moeq
+    from oracle import forward
+    from oracle.layer import OracleLayer
+    from synth import configs, gen
+    from tests import layers
+
+    cfg = configs.get("tiny")
+    E, H, I, G, r = cfg["E"], cfg["H"], cfg["I"], cfg["G"], cfg["r"]
+    bits = gen.gen_bits(cfg, 0)
+    blocks, fitted = [], {}
+    for e in range(E):
+        for blk in range(3):
+            W = torch.from_numpy(gen.gen_weight_block(cfg, 0, e, blk)).cuda()
+            q = moeq.quantize_block(W, "int", int(bits[e, blk]), G)
+            blocks.append(q)
+            l = min(r + 16, *W.shape)
+            omega = torch.from_numpy(gen.gen_test_matrix(cfg, 0, e, blk, l)).cuda()
+            U, V = moeq.fit_lowrank(W, q["codes"], q["scales"], q["zeros"], G, omega, r, 2)
+            fitted[(e, blk)] = (U.cpu().numpy(), V.cpu().numpy())
+    facs = [tuple(torch.from_numpy(a).cuda() for a in fitted[(e, b)]) for e in range(E) for b in range(3)]
+    dev = moeq.PackedLayer(E, H, I, G, "int", bits, blocks, facs)
+
+    def rows(e, blk, rr):
+        return gen.gen_weight_block(cfg, 0, e, blk) if rr is None else gen.gen_weight_rows(cfg, 0, e, blk, rr)
+
+    orc = OracleLayer(E, H, I, G, "int", bits, rows, factors=lambda e, blk: fitted[(e, blk)],
+                      cache_blocks=3 * E)
+    for e in range(E):
+        for blk in range(3):
+            W = gen.gen_weight_block(cfg, 0, e, blk).astype(np.float64)
+            R = W - forward.dequant_block(orc.qblock(e, blk), G)
+            U, V = (a.astype(np.float64) for a in fitted[(e, blk)])
+            assert np.linalg.norm(R - U @ V) < np.linalg.norm(R), (e, blk)
+    x, logits = gen.gen_x(cfg, 0), gen.gen_logits(cfg, 0)
+    rt = moeq.route(torch.from_numpy(logits).cuda(), cfg["k"])
+    y = moeq.expert_ffn(dev, torch.from_numpy(x).cuda(), rt, cfg["n_comp"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    layers.check_y(y.cpu().numpy(), layers.oracle_y(orc, cfg, x, logits, cfg["n_comp"]), "tiny, device-fitted factors")
