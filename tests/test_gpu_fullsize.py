@@ -24,9 +24,11 @@ def _sample_cols(H, n, seed):
     return np.array(sorted(cols))
 
 
-def _run_full(name, tokens, n_cols, seed=0, path=0):
+def _run_full(name, tokens, n_cols, seed=0, path=0, T=None):
     from bit_quantized_moe_token_amd import moeq
     cfg = configs.get(name)
+    if T is not None:
+        cfg = dict(cfg, T=T)
     x = gen.gen_x(cfg, seed)
     logits = gen.gen_logits(cfg, seed)
     dev = layers.device_layer(cfg, seed)
@@ -77,3 +79,13 @@ def test_bitplane_full_size_sampled_tiled():
     T = configs.get("bitplane")["T"]
     tokens = np.unique(np.concatenate([[0, 2, T - 2], np.linspace(0, T - 1, 5).astype(int)]))
     _run_full("bitplane", tokens, 192, path=3)
+
+
+@pytest.mark.timeout(600)
+def test_bitplane_prefill_full_size_sampled():
+    """The bit-plane layer with 4096 tokens (256 pairs per expert on
+    average), as the benchmark runs it: the default path is the tiled one
+    (three 128-token tiles for most experts, the last one partial)."""
+    T = 4096
+    tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 6).astype(int)]))
+    _run_full("bitplane", tokens, 160, T=T)
