@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--workload", choices=["decode", "prefill", "finegrained", "bitplane", "tiny"],
                    default="decode")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--tokens", type=int, default=0,
+                   help="run the workload's layer with this many tokens instead of its own T (the "
+                        "workload name and the summaries' file names follow)")
     p.add_argument("--path", type=int, default=0, help="moeq_path (0 = auto)")
     p.add_argument("--split-k", type=int, default=0, help="down-projection K splits (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -421,10 +424,10 @@ def summarize_sq(workload, trace_dir, sq_dir, stall_dir=None):
              "Two runs of the same command (a kernel trace, then one counter pass with "
              f"{' '.join(SQ_COUNTERS)}) and their reduction:", "", "```",
              f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o kt --output-format csv -- "
-             f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+             f"python3 bench.py {workload_ref(workload)[1]} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
              f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {sq_dir} -o pmc --output-format csv -- "
-             f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
-             f"python3 bench.py --workload {workload_short(workload)} --summarize-sq {trace_dir} {sq_dir}", "```", "",
+             f"python3 bench.py {workload_ref(workload)[1]} --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+             f"python3 bench.py {workload_ref(workload)[1]} --summarize-sq {trace_dir} {sq_dir}", "```", "",
              "Per dispatch (means). MFMA TFLOP/s = SQ_INSTS_MFMA x 16384 / mean duration (every MFMA here is "
              "16x16x32 fp16; padding rows and the low-rank MFMAs count). GRBM_GUI_ACTIVE sums the 8 XCDs' "
              "active cycles, so the clock = GRBM_GUI_ACTIVE / 8 / mean duration, and MFMA busy = "
@@ -451,7 +454,7 @@ def summarize_sq(workload, trace_dir, sq_dir, stall_dir=None):
         sv = _read_sq(stall_dir, SQ_STALL_COUNTERS)
         lines += ["", "Where the waves' cycles go, from a second counter pass of the same command:", "", "```",
                   f"rocprofv3 --pmc {' '.join(SQ_STALL_COUNTERS)} -d {stall_dir} -o pmc --output-format csv -- "
-                  f"python3 bench.py --workload {workload_short(workload)} --steps 5 --warmup 2 --no-cpu-baseline "
+                  f"python3 bench.py {workload_ref(workload)[1]} --steps 5 --warmup 2 --no-cpu-baseline "
                   f"--no-extra", "```", "",
                   "Shares of SQ_WAVE_CYCLES (the summed lifetime of the kernel's waves): issuing any instruction, "
                   "issuing VALU instructions (MFMAs included), waiting at a wait or barrier (SQ_WAIT_ANY), and "
@@ -472,7 +475,7 @@ def summarize_sq(workload, trace_dir, sq_dir, stall_dir=None):
                          f"{v.get('SQ_WAIT_INST_ANY', 0.0) / wc:.3f} | {v.get('SQ_INSTS_LDS', 0.0):.4g} | "
                          f"{(v.get('SQ_LDS_BANK_CONFLICT', 0.0) / lds) if lds else 0.0:.3f} |")
     lines.append("")
-    out = os.path.join(ROOT, "profiles", f"counters_{workload_short(workload)}.md")
+    out = os.path.join(ROOT, "profiles", f"counters_{workload_ref(workload)[0]}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
@@ -490,12 +493,12 @@ def summarize_trace(workload, trace_dir, top=30):
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     rows = list(csv.DictReader(open(stats[0])))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    short = workload_short(workload)
+    tag, wargs = workload_ref(workload)
     lines = [f"# Kernel time, {workload} (bench.py default command under rocprofv3)", "",
              "Commands (from the repository root, on one MI355X):", "", "```",
              f"cd /tmp && export TMPDIR=/tmp && cd - && rocprofv3 --kernel-trace --stats -d {trace_dir} -o kt "
              f"--output-format csv -- python3 bench.py --no-cpu-baseline",
-             f"python3 bench.py --workload {short} --summarize-trace {trace_dir}", "```", "",
+             f"python3 bench.py {wargs} --summarize-trace {trace_dir}", "```", "",
              "Source `kt_kernel_stats.csv`: every kernel of the run (the decode layer, the prefill layer, the "
              "tiny, fine-grained and bit-plane layers, and set-up: quantization, LUTs, packing), the "
              f"{top} largest by total time. Durations in microseconds.", "",
@@ -505,17 +508,24 @@ def summarize_trace(workload, trace_dir, top=30):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     lines.append("")
-    with open(os.path.join(ROOT, "profiles", f"kernels_{short}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"kernels_{tag}.md"), "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
 
-def workload_short(name):
+def workload_ref(name):
+    """(file-name tag, bench.py arguments) of a workload name: its short
+    name, with --tokens when the token count is not the config's own."""
+    import re
     from synth import configs
+    m = re.search(r"_t(\d+)_", name)
     for short in ("decode", "prefill", "finegrained", "bitplane", "tiny"):
-        if configs.get(short)["name"] == name:
-            return short
-    return name
+        base = configs.get(short)["name"]
+        if base == name:
+            return short, f"--workload {short}"
+        if m and re.sub(r"_t\d+_", f"_t{m.group(1)}_", base) == name:
+            return f"{short}_t{m.group(1)}", f"--workload {short} --tokens {m.group(1)}"
+    return name, f"--workload {name}"
 
 
 def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
@@ -541,9 +551,14 @@ def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(tr, fh, indent=1, sort_keys=True)
     print(json.dumps({workload: ent}, indent=1))
-    short = workload_short(workload)
+    tag, wargs = workload_ref(workload)
     rx = "gateup_kernel|down_kernel|lowrank|route|combine|neg_kernel"
-    cmd = (f"python3 bench.py --workload {short} --steps 20 --warmup 5 --no-cpu-baseline --no-extra "
+    steps, warmup = 20, 5
+    if bench_log and os.path.exists(bench_log):
+        # the step counts of the profiled run, from its bench line
+        b0 = json.loads([l for l in open(bench_log) if l.startswith("{")][-1])
+        steps, warmup = b0.get("steps", steps), b0.get("warmup", warmup)
+    cmd = (f"python3 bench.py {wargs} --steps {steps} --warmup {warmup} --no-cpu-baseline --no-extra "
            f"--copy-calibration")
     lines = [f"# HBM traffic per launch, {workload}", "",
              "Two counter passes (one counter each) and their reduction to bytes per launch:", "", "```",
@@ -551,7 +566,7 @@ def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
              f"--output-format csv -- {cmd}",
              f'rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "{rx}" -d {write_dir} -o pmc '
              f"--output-format csv -- {cmd}",
-             f"python3 bench.py --workload {short} --summarize-pmc {fetch_dir} {write_dir}"
+             f"python3 bench.py {wargs} --summarize-pmc {fetch_dir} {write_dir}"
              + (f" {bench_log}" if bench_log else ""), "```", "",
              f"The calibration kernel is an int8 negation over 1 GiB (reads and writes 2^30 B once each). "
              f"Scale factors (bytes per counted byte): FETCH_SIZE x{cf:.4f}, WRITE_SIZE x{cw:.4f}. "
@@ -573,7 +588,7 @@ def summarize_pmc(workload, fetch_dir, write_dir, bench_log=None):
             lines.append(f"Counter traffic of the gate/up launch over its algorithmic bytes: "
                          f"{gu['bytes'] / b['roofline']['bytes_per_launch']:.3f}.")
     lines.append("")
-    with open(os.path.join(ROOT, "profiles", f"traffic_{short}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.md"), "w") as fh:
         fh.write("\n".join(lines))
 
 
@@ -623,30 +638,37 @@ def cpu_baseline(cfg, seed, sample_tokens, min_seconds=12.0):
                        f"compensated SwiGLU FFN and combine ({dt:.1f} s)")
 
 
+def workload_cfg(args):
+    """The workload's config, with --tokens in place of its T (and in its name)."""
+    import re
+    from synth import configs
+    cfg = configs.get(args.workload)
+    if args.tokens > 0:
+        cfg = dict(cfg, T=args.tokens, name=re.sub(r"_t\d+_", f"_t{args.tokens}_", cfg["name"]))
+    return cfg
+
+
 def main():
     args = parse()
     if args.summarize_sq:
-        from synth import configs
-        summarize_sq(configs.get(args.workload)["name"], *args.summarize_sq)
+        summarize_sq(workload_cfg(args)["name"], *args.summarize_sq)
         return
     if args.summarize_pmc:
-        from synth import configs
-        summarize_pmc(configs.get(args.workload)["name"], *args.summarize_pmc)
+        summarize_pmc(workload_cfg(args)["name"], *args.summarize_pmc)
         return
     if args.summarize_trace:
-        from synth import configs
-        summarize_trace(configs.get(args.workload)["name"], args.summarize_trace)
+        summarize_trace(workload_cfg(args)["name"], args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the expert layer is not "
-              "sharded in this build", file=sys.stderr)
+              "sharded across GPUs", file=sys.stderr)
         sys.exit(2)
     import torch
     from synth import configs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg = configs.get(args.workload)
+    cfg = workload_cfg(args)
     t_setup = time.time()
     formats = {"main": cfg}
     copies = {"main": 3 if cfg["H"] * cfg["I"] * cfg["E"] > 1e8 else 2}
