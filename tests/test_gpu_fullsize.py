@@ -89,3 +89,14 @@ def test_bitplane_prefill_full_size_sampled():
     T = 4096
     tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 6).astype(int)]))
     _run_full("bitplane", tokens, 160, T=T)
+
+
+@pytest.mark.timeout(600)
+def test_int3_layer_prefill_batch_full_size_sampled():
+    """The int3 Mixtral-shaped decode layer (H 4096, I 14336, G128, rank 32,
+    outliers, Zipf-skewed routing) with a prefill batch of 2048 tokens
+    (512 pairs per expert on average): its default path is then the tiled
+    one, with the 3-bit field decode."""
+    T = 2048
+    tokens = np.unique(np.concatenate([[0, 1, T - 1], np.linspace(0, T - 1, 5).astype(int)]))
+    _run_full("decode", tokens, 192, T=T)
